@@ -1,0 +1,135 @@
+"""ctypes binding of libarrms.so (include/arrms.h), same names as the C ABI.
+
+Argument marshalling only: tensors become device pointers, the stream becomes
+the HIP stream handle, and a negative status becomes an ``ArrmsError``. Every
+step of the epilogue runs in the library's HIP kernels. Importing this module
+loads the library and raises ``ImportError`` when it has not been built
+(``python -m all_reduce_residual_rank_amd.build``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+# PyTorch-ROCm bundles its own HIP runtime (soname libamdhip64.so.7). Loading
+# torch first makes libarrms.so bind to that same runtime; loading the library
+# first would pull in /opt/rocm's runtime as a second copy, whose launches
+# reject torch's stream handles.
+try:
+    import torch  # noqa: F401
+except ImportError:  # pragma: no cover - torch is the memory/stream provider here
+    torch = None
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarrms.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                      "`python -m all_reduce_residual_rank_amd.build` (hipcc, gfx950)")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+# constants of include/arrms.h
+OK = 0
+ERR_INVALID = -1
+ERR_UNSUPPORTED = -2
+ERR_NO_STAGING = -3
+ERR_HIP = -4
+DTYPE_BF16, DTYPE_FP16, DTYPE_FP32 = 0, 1, 2
+GEMMA = 4
+FP8 = 8
+FORCE_ONE_STAGE = 16
+FORCE_TWO_STAGE = 32
+EXACT_ONLY = 64
+MAX_RANKS = 8
+MAX_HIDDEN = 16384
+DEFAULT_STAGING_BYTES = 16 << 20
+PATH_NONE, PATH_ONE_STAGE, PATH_TWO_STAGE = 0, 1, 2
+
+EXPORTS = ("arrms_fused", "arrms_reserve_staging", "arrms_release_staging",
+           "arrms_staging_bytes", "arrms_query_path", "arrms_status_string")
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_lib.arrms_fused.argtypes = [ctypes.POINTER(_vp), _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _vp]
+_lib.arrms_fused.restype = _i
+_lib.arrms_reserve_staging.argtypes = [_sz]
+_lib.arrms_reserve_staging.restype = _i
+_lib.arrms_release_staging.argtypes = []
+_lib.arrms_release_staging.restype = _i
+_lib.arrms_staging_bytes.argtypes = []
+_lib.arrms_staging_bytes.restype = _sz
+_lib.arrms_query_path.argtypes = [_i, _i, _i, _i]
+_lib.arrms_query_path.restype = _i
+_lib.arrms_status_string.argtypes = [_i]
+_lib.arrms_status_string.restype = ctypes.c_char_p
+
+LIB_PATH = _LIB_PATH
+
+
+class ArrmsError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status} ({arrms_status_string(status)})")
+        self.status = status
+
+
+def arrms_status_string(status: int) -> str:
+    return _lib.arrms_status_string(int(status)).decode()
+
+
+def _addr(t) -> int | None:
+    """Device address of a tensor (or an int address, or None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream_handle(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def arrms_fused_raw(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale,
+                    M, H, eps, flags, stream) -> int:
+    """The C call with addresses as ints; returns the status unchanged."""
+    ptrs = (_vp * max(len(rank_in), 1))(*[_addr(p) for p in rank_in])
+    return _lib.arrms_fused(ptrs, int(R), _addr(residual), _addr(weight), _addr(out),
+                            _addr(residual_out), _addr(fp8_out), _addr(fp8_scale), int(M), int(H),
+                            float(eps), int(flags), stream)
+
+
+def arrms_fused(rank_in, residual, weight, out, residual_out, fp8_out=None, fp8_scale=None, *,
+                eps: float, flags: int, M: int | None = None, H: int | None = None, stream=None) -> None:
+    """Enqueue the fused epilogue on ``stream`` (default: torch's current stream).
+
+    rank_in: list of R device tensors [M][H] (or addresses); the other arguments
+    as in include/arrms.h. M and H default to the residual's shape.
+    """
+    if M is None or H is None:
+        M, H = residual.shape[-2], residual.shape[-1]
+    st = _stream_handle(stream)
+    rc = arrms_fused_raw(rank_in, len(rank_in), residual, weight, out, residual_out, fp8_out,
+                         fp8_scale, M, H, eps, flags, st)
+    if rc != OK:
+        raise ArrmsError(rc, "arrms_fused")
+
+
+def arrms_reserve_staging(nbytes: int = 0) -> None:
+    rc = _lib.arrms_reserve_staging(int(nbytes))
+    if rc != OK:
+        raise ArrmsError(rc, "arrms_reserve_staging")
+
+
+def arrms_release_staging() -> None:
+    rc = _lib.arrms_release_staging()
+    if rc != OK:
+        raise ArrmsError(rc, "arrms_release_staging")
+
+
+def arrms_staging_bytes() -> int:
+    return int(_lib.arrms_staging_bytes())
+
+
+def arrms_query_path(M: int, H: int, R: int, flags: int) -> int:
+    return int(_lib.arrms_query_path(int(M), int(H), int(R), int(flags)))

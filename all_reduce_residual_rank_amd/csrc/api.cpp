@@ -1,0 +1,414 @@
+// api.cpp -- the C ABI of libarrms.so (include/arrms.h): argument checks,
+// path and launch-shape choice, the staging buffer, and the launches.
+//
+// Path choice follows ROCm/aiter PR #6699 "gfx1250 fused all-reduce +
+// RMSNorm" (section Changes): a direct-read one-stage kernel, and an exact
+// two-stage path (reduce into a staging region, then a row pass applying the
+// residual and the norm) that the collective prefers for wide rows. On one
+// GPU both read the same R inputs; the thresholds here come from measurement
+// on MI355X, not from the pages' multi-GPU numbers.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "arrms.h"
+#include "launch.hpp"
+
+namespace {
+
+using arrms::DT_BF16;
+using arrms::DT_FP16;
+using arrms::DT_FP32;
+
+constexpr int kKnownFlags = ARRMS_DTYPE_MASK | ARRMS_GEMMA | ARRMS_FP8 | ARRMS_FORCE_ONE_STAGE |
+                            ARRMS_FORCE_TWO_STAGE | ARRMS_EXACT_ONLY;
+constexpr int kMaxDevices = 64;
+
+int esize(int dt) { return dt == DT_FP32 ? 4 : 2; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlaps(const Span &a, const Span &b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Checks that need no device: sizes, flags, pointers, alignment, overlap.
+int validate(const void *const *rank_in, int R, const void *residual, const void *weight,
+             const void *out, const void *residual_out, const void *fp8_out,
+             const float *fp8_scale, int M, int H, float eps, int flags)
+{
+    if (flags & ~kKnownFlags)
+        return ARRMS_ERR_INVALID;
+    const int dt = flags & ARRMS_DTYPE_MASK;
+    if (dt > DT_FP32)
+        return ARRMS_ERR_INVALID;
+    if ((flags & ARRMS_FORCE_ONE_STAGE) && (flags & ARRMS_FORCE_TWO_STAGE))
+        return ARRMS_ERR_INVALID;
+    if (R < 1 || R > ARRMS_MAX_RANKS || M < 0 || H < 1)
+        return ARRMS_ERR_INVALID;
+    if (!(eps >= 0.0f) || eps > 3.4028234e38f)  // rejects NaN, negative, +inf
+        return ARRMS_ERR_INVALID;
+    const bool fp8 = (flags & ARRMS_FP8) != 0;
+    if (!rank_in || !residual || !weight || !residual_out)
+        return ARRMS_ERR_INVALID;
+    for (int r = 0; r < R; ++r)
+        if (!rank_in[r])
+            return ARRMS_ERR_INVALID;
+    if (!fp8 && !out)
+        return ARRMS_ERR_INVALID;
+    if (fp8 && (!fp8_out || !fp8_scale))
+        return ARRMS_ERR_INVALID;
+    if (H > ARRMS_MAX_HIDDEN)
+        return ARRMS_ERR_UNSUPPORTED;
+    if (fp8 && dt == DT_FP32)
+        return ARRMS_ERR_UNSUPPORTED;
+    if (((long long)H * esize(dt)) % 16 != 0)
+        return ARRMS_ERR_UNSUPPORTED;
+    for (int r = 0; r < R; ++r)
+        if (!aligned16(rank_in[r]))
+            return ARRMS_ERR_UNSUPPORTED;
+    if (!aligned16(residual) || !aligned16(weight) || !aligned16(residual_out) ||
+        (out && !aligned16(out)))
+        return ARRMS_ERR_UNSUPPORTED;
+    if (fp8 && (!aligned16(fp8_out) || ((uintptr_t)fp8_scale & 3u)))
+        return ARRMS_ERR_UNSUPPORTED;
+
+    // overlap: outputs against inputs and against each other
+    const uintptr_t mat = (uintptr_t)M * (uintptr_t)H * (uintptr_t)esize(dt);
+    if (M == 0)
+        return ARRMS_OK;
+    Span ins[ARRMS_MAX_RANKS + 2];
+    int nin = 0;
+    for (int r = 0; r < R; ++r)
+        ins[nin++] = {(uintptr_t)rank_in[r], (uintptr_t)rank_in[r] + mat};
+    const Span res_span = {(uintptr_t)residual, (uintptr_t)residual + mat};
+    ins[nin++] = {(uintptr_t)weight, (uintptr_t)weight + (uintptr_t)H * esize(dt)};
+    Span outs[4];
+    int nout = 0;
+    const bool inplace = residual_out == residual;
+    outs[nout++] = {(uintptr_t)residual_out, (uintptr_t)residual_out + mat};
+    if (out)
+        outs[nout++] = {(uintptr_t)out, (uintptr_t)out + mat};
+    if (fp8) {
+        outs[nout++] = {(uintptr_t)fp8_out, (uintptr_t)fp8_out + (uintptr_t)M * (uintptr_t)H};
+        outs[nout++] = {(uintptr_t)fp8_scale, (uintptr_t)fp8_scale + (uintptr_t)M * 4u};
+    }
+    for (int o = 0; o < nout; ++o) {
+        for (int i = 0; i < nin; ++i)
+            if (overlaps(outs[o], ins[i]))
+                return ARRMS_ERR_INVALID;
+        const bool is_res_out = o == 0;
+        if (!(is_res_out && inplace) && overlaps(outs[o], res_span))
+            return ARRMS_ERR_INVALID;
+        for (int p = o + 1; p < nout; ++p)
+            if (overlaps(outs[o], outs[p]))
+                return ARRMS_ERR_INVALID;
+    }
+    return ARRMS_OK;
+}
+
+int validate_sizes(int M, int H, int R, int flags)
+{
+    if (flags & ~kKnownFlags)
+        return ARRMS_ERR_INVALID;
+    const int dt = flags & ARRMS_DTYPE_MASK;
+    if (dt > DT_FP32)
+        return ARRMS_ERR_INVALID;
+    if ((flags & ARRMS_FORCE_ONE_STAGE) && (flags & ARRMS_FORCE_TWO_STAGE))
+        return ARRMS_ERR_INVALID;
+    if (R < 1 || R > ARRMS_MAX_RANKS || M < 0 || H < 1)
+        return ARRMS_ERR_INVALID;
+    if (H > ARRMS_MAX_HIDDEN)
+        return ARRMS_ERR_UNSUPPORTED;
+    if ((flags & ARRMS_FP8) && dt == DT_FP32)
+        return ARRMS_ERR_UNSUPPORTED;
+    if (((long long)H * esize(dt)) % 16 != 0)
+        return ARRMS_ERR_UNSUPPORTED;
+    return ARRMS_OK;
+}
+
+int choose_path(int M, int H, int R, int flags)
+{
+    (void)H;
+    (void)R;
+    if (M == 0)
+        return ARRMS_PATH_NONE;
+    if (flags & ARRMS_FORCE_TWO_STAGE)
+        return ARRMS_PATH_TWO_STAGE;
+    if (flags & ARRMS_FORCE_ONE_STAGE)
+        return ARRMS_PATH_ONE_STAGE;
+    // One GPU: the one-stage kernel moves the fewest bytes (R inputs + residual
+    // in, two outputs); two-stage adds a staging write and read.
+    return ARRMS_PATH_ONE_STAGE;
+}
+
+// Row-kernel shape for P packs per row: PPT in {1,2,4,8} (bounded by the
+// register budget for R+1 streams), tpr = PPT-covering multiple of 64 up to
+// 512. Prefer an exact cover (no tail), then the least padding, then tpr
+// nearest 256.
+arrms::RowShape choose_shape(int P, int R, long long M)
+{
+    arrms::RowShape best = {0, 0, 0, false, 0};
+    long long best_key = -1;
+    const int ppts[4] = {1, 2, 4, 8};
+    for (int c = 0; c < 4; ++c) {
+        const int ppt = ppts[c];
+        if (ppt * (R + 1) > 45)
+            continue;
+        int tpr = (P + ppt - 1) / ppt;
+        tpr = (tpr + 63) / 64 * 64;
+        if (tpr > 512)
+            continue;
+        const int waste = tpr * ppt - P;
+        const int dist = tpr > 256 ? tpr - 256 : 256 - tpr;
+        const long long key = (long long)waste * 4096 + dist;
+        if (best_key < 0 || key < best_key) {
+            best_key = key;
+            best = {ppt, tpr, 1, waste != 0, 0};
+        }
+    }
+    if (best.ppt == 0)
+        return best;
+    best.rpb = best.tpr >= 256 ? 1 : 256 / best.tpr;
+    const long long groups = (M + best.rpb - 1) / best.rpb;
+    const long long cap = 256LL * 32;  // grid-stride beyond this
+    best.grid = (int)(groups < cap ? groups : cap);
+    if (best.grid < 1)
+        best.grid = 1;
+    return best;
+}
+
+hipError_t launch_row(int dt, const arrms::RowArgs &a, int R, const arrms::RowShape &s,
+                      hipStream_t st)
+{
+    switch (dt) {
+    case DT_BF16: return arrms::launch_row_bf16(a, R, s, st);
+    case DT_FP16: return arrms::launch_row_fp16(a, R, s, st);
+    default: return arrms::launch_row_fp32(a, R, s, st);
+    }
+}
+
+hipError_t launch_flat(int dt, const arrms::FlatArgs &a, int R, hipStream_t st)
+{
+    switch (dt) {
+    case DT_BF16: return arrms::launch_flat_bf16(a, R, st);
+    case DT_FP16: return arrms::launch_flat_fp16(a, R, st);
+    default: return arrms::launch_flat_fp32(a, R, st);
+    }
+}
+
+// ---- staging buffer: one per device, owned by the library ----------------
+struct Staging {
+    void *ptr;
+    size_t bytes;
+};
+std::mutex g_staging_mu;
+Staging g_staging[kMaxDevices];
+
+int reserve_locked(int dev, size_t bytes)
+{
+    if (g_staging[dev].bytes >= bytes && g_staging[dev].ptr)
+        return ARRMS_OK;
+    void *p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return ARRMS_ERR_HIP;
+    }
+    if (g_staging[dev].ptr) {
+        if (hipDeviceSynchronize() != hipSuccess || hipFree(g_staging[dev].ptr) != hipSuccess) {
+            (void)hipFree(p);
+            (void)hipGetLastError();
+            return ARRMS_ERR_HIP;
+        }
+    }
+    g_staging[dev].ptr = p;
+    g_staging[dev].bytes = bytes;
+    return ARRMS_OK;
+}
+
+int current_device(int *dev)
+{
+    if (hipGetDevice(dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return ARRMS_ERR_HIP;
+    }
+    if (*dev < 0 || *dev >= kMaxDevices)
+        return ARRMS_ERR_HIP;
+    return ARRMS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *arrms_status_string(int status)
+{
+    switch (status) {
+    case ARRMS_OK: return "ok";
+    case ARRMS_ERR_INVALID: return "invalid argument (pointer, size, flags or overlap)";
+    case ARRMS_ERR_UNSUPPORTED:
+        return "unsupported layout (alignment, H*sizeof(T) % 16, FP8 with fp32, H too large)";
+    case ARRMS_ERR_NO_STAGING: return "two-stage path inside stream capture without reserved staging";
+    case ARRMS_ERR_HIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+    }
+}
+
+int arrms_query_path(int M, int H, int R, int flags)
+{
+    const int v = validate_sizes(M, H, R, flags);
+    if (v != ARRMS_OK)
+        return v;
+    return choose_path(M, H, R, flags);
+}
+
+int arrms_reserve_staging(size_t bytes)
+{
+    int dev;
+    int rc = current_device(&dev);
+    if (rc != ARRMS_OK)
+        return rc;
+    if (bytes == 0)
+        bytes = ARRMS_DEFAULT_STAGING_BYTES;
+    std::lock_guard<std::mutex> lk(g_staging_mu);
+    return reserve_locked(dev, bytes);
+}
+
+int arrms_release_staging(void)
+{
+    int dev;
+    int rc = current_device(&dev);
+    if (rc != ARRMS_OK)
+        return rc;
+    std::lock_guard<std::mutex> lk(g_staging_mu);
+    if (!g_staging[dev].ptr)
+        return ARRMS_OK;
+    if (hipDeviceSynchronize() != hipSuccess || hipFree(g_staging[dev].ptr) != hipSuccess) {
+        (void)hipGetLastError();
+        return ARRMS_ERR_HIP;
+    }
+    g_staging[dev].ptr = nullptr;
+    g_staging[dev].bytes = 0;
+    return ARRMS_OK;
+}
+
+size_t arrms_staging_bytes(void)
+{
+    int dev;
+    if (current_device(&dev) != ARRMS_OK)
+        return 0;
+    std::lock_guard<std::mutex> lk(g_staging_mu);
+    return g_staging[dev].ptr ? g_staging[dev].bytes : 0;
+}
+
+int arrms_fused(const void *const *rank_in, int R, const void *residual, const void *weight,
+                void *out, void *residual_out, void *fp8_out, float *fp8_scale, int M, int H,
+                float eps, int flags, hipStream_t stream)
+{
+    int rc = validate(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H,
+                      eps, flags);
+    if (rc != ARRMS_OK)
+        return rc;
+    const int path = choose_path(M, H, R, flags);
+    if (path == ARRMS_PATH_NONE)
+        return ARRMS_OK;
+
+    const int dt = flags & ARRMS_DTYPE_MASK;
+    const int e = esize(dt);
+    const int P = H * e / 16;
+    const bool fp8 = (flags & ARRMS_FP8) != 0;
+
+    arrms::RowArgs a;
+    memset(&a, 0, sizeof(a));
+    a.residual = residual;
+    a.weight = weight;
+    a.out = out;
+    a.residual_out = residual_out;
+    a.fp8_out = fp8 ? fp8_out : nullptr;
+    a.fp8_scale = fp8 ? fp8_scale : nullptr;
+    a.P = P;
+    a.H = H;
+    a.eps = eps;
+    a.gemma = (flags & ARRMS_GEMMA) != 0;
+    a.fp8 = fp8;
+    a.exact_only = (flags & ARRMS_EXACT_ONLY) != 0;
+
+    (void)hipGetLastError();  // launches below report their own errors
+    if (path == ARRMS_PATH_ONE_STAGE) {
+        for (int r = 0; r < R; ++r)
+            a.in[r] = rank_in[r];
+        a.M = M;
+        arrms::RowShape s = choose_shape(P, R, M);
+        if (s.ppt == 0)
+            return ARRMS_ERR_UNSUPPORTED;
+        a.tpr = s.tpr;
+        return launch_row(dt, a, R, s, stream) == hipSuccess ? ARRMS_OK : ARRMS_ERR_HIP;
+    }
+
+    // ---- two-stage: per row chunk, flat rank reduce into staging, then the
+    // row pass with the staging rows as its single input.
+    int dev;
+    rc = current_device(&dev);
+    if (rc != ARRMS_OK)
+        return rc;
+    void *staging;
+    size_t staging_bytes;
+    {
+        std::lock_guard<std::mutex> lk(g_staging_mu);
+        if (!g_staging[dev].ptr) {
+            hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+            if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+                (void)hipGetLastError();
+                return ARRMS_ERR_HIP;
+            }
+            if (cs != hipStreamCaptureStatusNone)
+                return ARRMS_ERR_NO_STAGING;
+            rc = reserve_locked(dev, ARRMS_DEFAULT_STAGING_BYTES);
+            if (rc != ARRMS_OK)
+                return rc;
+        }
+        staging = g_staging[dev].ptr;
+        staging_bytes = g_staging[dev].bytes;
+    }
+    const size_t row_bytes = (size_t)H * (size_t)e;
+    long long chunk = (long long)(staging_bytes / row_bytes);
+    if (chunk < 1)
+        return ARRMS_ERR_NO_STAGING;
+    for (long long m0 = 0; m0 < M; m0 += chunk) {
+        const long long n = (M - m0) < chunk ? (M - m0) : chunk;
+        const size_t off = (size_t)m0 * row_bytes;
+        arrms::FlatArgs f;
+        memset(&f, 0, sizeof(f));
+        for (int r = 0; r < R; ++r)
+            f.in[r] = (const char *)rank_in[r] + off;
+        f.dst = staging;
+        f.npacks = n * P;
+        if (launch_flat(dt, f, R, stream) != hipSuccess)
+            return ARRMS_ERR_HIP;
+        arrms::RowArgs b = a;
+        b.in[0] = staging;
+        b.residual = (const char *)residual + off;
+        b.residual_out = (char *)residual_out + off;
+        b.out = out ? (char *)out + off : nullptr;
+        if (fp8) {
+            b.fp8_out = (char *)fp8_out + (size_t)m0 * (size_t)H;
+            b.fp8_scale = fp8_scale + m0;
+        }
+        b.M = n;
+        // the row pass takes the one-stage shape of these rows, so both paths
+        // reduce the row statistics in the same order and give the same bits
+        const arrms::RowShape s = choose_shape(P, R, n);
+        if (s.ppt == 0)
+            return ARRMS_ERR_UNSUPPORTED;
+        b.tpr = s.tpr;
+        if (launch_row(dt, b, 1, s, stream) != hipSuccess)
+            return ARRMS_ERR_HIP;
+    }
+    return ARRMS_OK;
+}
+
+}  // extern "C"

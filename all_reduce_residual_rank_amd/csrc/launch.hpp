@@ -1,0 +1,64 @@
+// launch.hpp -- internal interface between the C ABI (api.cpp) and the
+// per-dtype kernel translation units (kern_bf16.hip, kern_fp16.hip,
+// kern_fp32.hip). Not installed; not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace arrms {
+
+enum Dtype { DT_BF16 = 0, DT_FP16 = 1, DT_FP32 = 2 };
+
+constexpr int kMaxRanks = 8;
+constexpr int kMaxWavesPerBlock = 8;   // row kernel blocks are at most 512 threads
+
+// Arguments of the row kernel (one-stage, and stage 2 of two-stage with R = 1
+// and the staging buffer as its only input). Pointers are to 16-byte packs.
+struct RowArgs {
+    const void *in[kMaxRanks];
+    const void *residual;
+    const void *weight;
+    void *out;            // may be null when fp8 is set (no T mirror)
+    void *residual_out;
+    void *fp8_out;        // bytes, [M][H]
+    float *fp8_scale;     // [M]
+    long long M;          // rows
+    int P;                // 16-byte packs per row
+    int H;                // elements per row
+    int tpr;              // threads per row group (multiple of 64)
+    float eps;
+    int gemma;
+    int fp8;
+    int exact_only;
+};
+
+// Arguments of the flat rank reduce (stage 1 of two-stage).
+struct FlatArgs {
+    const void *in[kMaxRanks];
+    void *dst;
+    long long npacks;     // packs to reduce
+};
+
+// Row kernel shape: PPT packs per thread per row, tpr threads per row,
+// rpb rows per block; tail = tpr * PPT > packs per row.
+struct RowShape {
+    int ppt;
+    int tpr;
+    int rpb;
+    bool tail;
+    int grid;
+};
+
+constexpr int kFlatThreads = 256;
+constexpr int kFlatPacksPerThread = 2;
+constexpr int kFlatTile = kFlatThreads * kFlatPacksPerThread;
+
+hipError_t launch_row_bf16(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
+hipError_t launch_row_fp16(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
+hipError_t launch_row_fp32(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
+hipError_t launch_flat_bf16(const FlatArgs &a, int R, hipStream_t st);
+hipError_t launch_flat_fp16(const FlatArgs &a, int R, hipStream_t st);
+hipError_t launch_flat_fp32(const FlatArgs &a, int R, hipStream_t st);
+
+}  // namespace arrms

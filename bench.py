@@ -1,0 +1,254 @@
+"""Benchmark of the fused rank-sum + residual-add + RMSNorm epilogue on one MI355X.
+
+One step = one arrms_fused call over the headline workload (R=4 rank inputs,
+1024 x 6144 bf16 rows, per-row input scales, plain RMSNorm, bf16 output),
+with its inputs already resident in HBM. The timed calls cycle through enough
+rotating buffer sets (>= 512 MiB in total, twice the 256 MB Infinity Cache) that
+every call reads cold data from HBM. Calls are captured in a HIP graph and
+timed with HIP events on the stream the kernels run on.
+
+Prints one JSON line:
+  value       achieved GB/s by the metric's byte count (R+2)*M*H*2 + H*2
+  roofline    algorithmic bytes per launch ((R+3)*M*H*e + H*e: R inputs and the
+              residual read, out and residual_out written, the weight) over the
+              measured kernel duration, against MI355X's 8 TB/s HBM peak
+  cpu_baseline  the CPU oracle, single-threaded, on the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs/call and achieved HBM GB/s (% of peak) for fused sum+RMSNorm, R=4, H=6144"
+PEAK_GBS = 8000.0
+ROTATE_BYTES = 512 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=256)
+    p.add_argument("--warmup", type=int, default=32)
+    p.add_argument("--workload", default="r4_m1024_h6144_bf16_rowscale")
+    p.add_argument("--path", choices=("auto", "one", "two"), default="auto")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="bound on the CPU-baseline work")
+    p.add_argument("--quiet", action="store_true")
+    return p.parse_args()
+
+
+def sources_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "all_reduce_residual_rank_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, path: str, digest: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they were
+    taken on the current kernel sources; else None."""
+    f = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(f):
+        return None
+    try:
+        d = json.load(open(f))
+    except (OSError, ValueError):
+        return None
+    e = d.get(f"{workload}/{path}")
+    if not e or e.get("sources_digest") != digest:
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+class Sets:
+    """Rotating device buffer sets of one workload."""
+
+    def __init__(self, wl, nsets, torch):
+        from all_reduce_residual_rank_amd import workloads as wlmod
+        dev = torch.device("cuda")
+        T = wlmod.DTYPES[wl.dtype]
+        xs, res, w = wlmod.make_inputs(wl, seed=0)
+        self.sets = []
+        for s in range(nsets):
+            d = {"xs": [x.to(dev) for x in xs], "res": res.to(dev), "w": w.to(dev),
+                 "rout": torch.empty(wl.M, wl.H, dtype=T, device=dev),
+                 "out": torch.empty(wl.M, wl.H, dtype=T, device=dev) if (wl.mirror or not wl.fp8) else None,
+                 "q": torch.empty(wl.M, wl.H, dtype=torch.uint8, device=dev) if wl.fp8 else None,
+                 "sc": torch.empty(wl.M, dtype=torch.float32, device=dev) if wl.fp8 else None}
+            self.sets.append(d)
+
+
+def call(arrms, wl, d, flags, stream):
+    arrms.arrms_fused(d["xs"], d["res"], d["w"], d["out"], d["rout"], d["q"], d["sc"], eps=wl.eps,
+                      flags=flags, M=wl.M, H=wl.H, stream=stream)
+
+
+def time_path(torch, arrms, wl, sets, flags, steps, warmup):
+    """Warm up, then time exactly `steps` calls replayed from one HIP graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    n = len(sets.sets)
+    gw = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gw, stream=s):
+        for i in range(warmup):
+            call(arrms, wl, sets.sets[i % n], flags, s)
+    gk = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gk, stream=s):
+        for i in range(steps):
+            call(arrms, wl, sets.sets[i % n], flags, s)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        gw.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        e0.record(s)
+        gk.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    del gw, gk
+    return ms
+
+
+def time_hot(torch, arrms, wl, sets, flags, reps=64):
+    """Single buffer set replayed: cache-resident ("hot") context number."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(reps):
+            call(arrms, wl, sets.sets[0], flags, s)
+    torch.cuda.synchronize()
+    res = []
+    for _ in range(5):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):
+            e0.record(s)
+            g.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) * 1000.0 / reps)
+    return min(res)
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle as it stands, single-threaded, on row samples of the workload."""
+    import numpy as np
+    import torch
+    import oracle
+    from all_reduce_residual_rank_amd import workloads as wlmod
+
+    xs, res, w = wlmod.make_inputs(wl, seed=0)
+
+    def bits(t):
+        if t.dtype == torch.float32:
+            return t.numpy()
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    xb = [bits(x) for x in xs]
+    rb, wb = bits(res), bits(w)
+    def once(n):
+        t0 = time.perf_counter()
+        oracle.fused(xb, rb, wb, wl.eps, wl.flags & 0xF, rows=(0, n))
+        return time.perf_counter() - t0
+
+    probe = min(wl.M, 8)
+    t_probe = once(probe)
+    rows = max(1, min(wl.M, int(probe * (budget_s / 3.0) / max(t_probe, 1e-9))))
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 or (len(times) < 15 and time.perf_counter() - t_start < budget_s):
+        times.append(once(rows))
+    t = statistics.median(times)
+    e = wl.esize
+    metric_bytes = (wl.R + 2) * rows * wl.H * e + wl.H * e
+    return {"value": round(metric_bytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the workload ({rows}x{wl.H}, R={wl.R}), "
+                      f"median of {len(times)} runs, {t * 1e3:.1f} ms each",
+            "us_per_row": round(t / rows * 1e6, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    from all_reduce_residual_rank_amd import arrms
+    from all_reduce_residual_rank_amd import workloads as wlmod
+
+    wl = wlmod.BY_NAME[args.workload]
+    torch.cuda.set_device(0)
+    e = wl.esize
+    set_bytes = (wl.R + 3) * wl.M * wl.H * e
+    nsets = max(2, -(-ROTATE_BYTES // set_bytes))
+    sets = Sets(wl, nsets, torch)
+    arrms.arrms_reserve_staging(0)
+
+    path_flags = {"one": arrms.FORCE_ONE_STAGE, "two": arrms.FORCE_TWO_STAGE, "auto": 0}
+    auto_path = {arrms.PATH_ONE_STAGE: "one", arrms.PATH_TWO_STAGE: "two"}[
+        arrms.arrms_query_path(wl.M, wl.H, wl.R, wl.flags)]
+    chosen = auto_path if args.path == "auto" else args.path
+    ms = time_path(torch, arrms, wl, sets, wl.flags | path_flags[chosen], args.steps, args.warmup)
+    us = ms * 1000.0 / args.steps
+    metric_bytes = (wl.R + 2) * wl.M * wl.H * e + wl.H * e
+    algo_bytes = (wl.R + 3) * wl.M * wl.H * e + wl.H * e
+    if wl.fp8:
+        algo_bytes = (wl.R + 1) * wl.M * wl.H * e + wl.H * e + wl.M * wl.H + wl.M * 4 + \
+            (wl.M * wl.H * e if wl.mirror else 0) + wl.M * wl.H * e
+    gbs = metric_bytes / (us * 1e-6) / 1e9
+    achieved = algo_bytes / (us * 1e-6) / 1e9
+
+    other = {}
+    for p in ("one", "two"):
+        if p == chosen:
+            other[p] = round(us, 3)
+        else:
+            ms2 = time_path(torch, arrms, wl, sets, wl.flags | path_flags[p], args.steps, args.warmup)
+            other[p] = round(ms2 * 1000.0 / args.steps, 3)
+    hot = time_hot(torch, arrms, wl, sets, wl.flags | path_flags[chosen])
+    digest = sources_digest()
+    traffic = load_traffic(wl.name, chosen, digest)
+
+    line = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms / args.steps, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "R": wl.R, "M": wl.M, "H": wl.H, "dtype": wl.dtype,
+                   "gemma": wl.gemma, "fp8": wl.fp8, "path": chosen, "rotating_sets": nsets,
+                   "compute": "fp32 rank sums, fp64 row statistics"},
+        "us_per_call": round(us, 3), "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
+        "metric_bytes": metric_bytes,
+        "path_us": other, "hot_us_cache_resident": round(hot, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": algo_bytes,
+                     "kernel": "row_kernel" if chosen == "one" else "flat_kernel+row_kernel"},
+        "sources_digest": digest,
+        "device": torch.cuda.get_device_name(0),
+        "arch": torch.cuda.get_device_properties(0).gcnArchName,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,147 @@
+/*
+ * arrms.h -- fused rank-sum + residual-add + RMSNorm (+ per-token FP8 E4M3)
+ * epilogue for MI355X (gfx950), C ABI of libarrms.so.
+ *
+ * The operation is the epilogue of a tensor-parallel all-reduce, taken as the
+ * share of work one GPU can show: R rank-input buffers, all resident in this
+ * GPU's HBM, stand in for the peer-visible registered buffers of the
+ * collective. Sources: ROCm/aiter PR #6699 "gfx1250 fused all-reduce +
+ * RMSNorm" (sections Changes and Test results, and the commit notes), PR
+ * #3462 "optimize fused AllReduce + RMSNorm" (section Technical Details), PR
+ * #5807 "Specialize partial tiles in two-stage custom all-reduce" (section
+ * Proposed modifications).
+ *
+ * Every entry point is a plain C function; buffers are raw pointers, sizes
+ * are ints, the stream is a HIP stream handle. Nothing here prints, throws or
+ * aborts: failures come back as a negative status (see ARRMS_ERR_*), and on
+ * any failure nothing has been launched and no output has been written.
+ */
+#ifndef ARRMS_H
+#define ARRMS_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef ARRMS_API
+#define ARRMS_API __attribute__((visibility("default")))
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define ARRMS_OK 0
+#define ARRMS_ERR_INVALID (-1)     /* NULL required pointer, R/M/H out of range, bad flags, overlap */
+#define ARRMS_ERR_UNSUPPORTED (-2) /* misaligned pointer, H*sizeof(T) not a multiple of 16 bytes,
+                                      FP8 with fp32 data: the caller takes its unfused path,
+                                      as the communicator on the pages does for padded rows */
+#define ARRMS_ERR_NO_STAGING (-3)  /* two-stage path needed inside stream capture, no staging reserved */
+#define ARRMS_ERR_HIP (-4)         /* a HIP runtime call or kernel launch failed */
+
+/* ---- flags (bit field) ------------------------------------------------ */
+#define ARRMS_DTYPE_BF16 0         /* bits 0-1: element type T of inputs, residual, weight, outputs */
+#define ARRMS_DTYPE_FP16 1
+#define ARRMS_DTYPE_FP32 2
+#define ARRMS_DTYPE_MASK 3
+#define ARRMS_GEMMA 4              /* scale by (1 + w) instead of w (gemma_norm, PR #6699 Changes) */
+#define ARRMS_FP8 8                /* per-token FP8 E4M3 output + fp32 per-row scales (PR #6699 Changes) */
+#define ARRMS_FORCE_ONE_STAGE 16   /* force the one-stage direct-read path */
+#define ARRMS_FORCE_TWO_STAGE 32   /* force the two-stage path (flat rank reduce into staging, then row pass) */
+#define ARRMS_EXACT_ONLY 64        /* verification: take the exact rounding branch for every element
+                                      (same results; used to check the fast branches bit for bit) */
+
+/* ---- limits -------------------------------------------------------------- */
+#define ARRMS_MAX_RANKS 8          /* the pages go up to TP8 (PR #3462 Test Results) */
+#define ARRMS_MAX_HIDDEN 16384
+#define ARRMS_DEFAULT_STAGING_BYTES (16u << 20) /* 16 MiB staging region (PR #6699 Changes) */
+
+/* ---- paths returned by arrms_query_path ---------------------------------- */
+#define ARRMS_PATH_NONE 0          /* M == 0: nothing to launch */
+#define ARRMS_PATH_ONE_STAGE 1
+#define ARRMS_PATH_TWO_STAGE 2
+
+/*
+ * arrms_fused -- the fused epilogue (PR #6699 Changes: direct-read one-stage
+ * and exact two-stage fused kernels; PR #3462 Technical Details: rank-ordered
+ * fp32 reduce).
+ *
+ * For every row m < M and column j < H, with T the type named by flags:
+ *   a      = RNE_T( x_0 + x_1 + ... + x_{R-1} )      fp32 adds in rank order 0..R-1,
+ *                                                    accumulator starting at x_0
+ *   h      = RNE_T( fl32(a + residual) )             -> residual_out[m][j]
+ *   rstd   = 1 / sqrt( sum_j h^2 / H + eps )         statistics in fp64
+ *   y      = RNE_T( (h * w_eff) * rstd )             w_eff = w, or 1 + w with ARRMS_GEMMA;
+ *                                                    one rounding from fp64 -> out[m][j]
+ *   FP8:   amax = max_j |y| ; scale = fl32(amax / 448) -> fp8_scale[m]
+ *          q = E4M3_RNE_saturating( fl32(y / scale) ) -> fp8_out[m][j]
+ *          (amax == 0 gives scale 0 and q = +-0 with the sign of y)
+ * For T = fp32 the two RNE_T steps before the norm are the fp32 operations.
+ *
+ * rank_in      host array of R device pointers, each to [M][H] T (row-major,
+ *              contiguous). The array is read during the call and its values
+ *              are baked into the launch (and into a captured graph); the
+ *              caller may reuse it after return. Rank pointers may repeat.
+ * R            1 .. ARRMS_MAX_RANKS.
+ * residual     device [M][H] T.
+ * weight       device [H] T.
+ * out          device [M][H] T. Required without ARRMS_FP8; with ARRMS_FP8 it is
+ *              the optional T mirror of the quantised output (NULL: not written).
+ * residual_out device [M][H] T; may equal residual exactly (in place).
+ * fp8_out      device [M][H] bytes (E4M3 codes), required with ARRMS_FP8, else ignored.
+ * fp8_scale    device [M] float, required with ARRMS_FP8, else ignored.
+ * M            rows, >= 0 (0: returns ARRMS_OK, launches nothing).
+ * H            hidden size, 1 .. ARRMS_MAX_HIDDEN, with H * sizeof(T) % 16 == 0.
+ * eps          finite, >= 0.
+ * flags        ARRMS_DTYPE_* | ARRMS_GEMMA | ARRMS_FP8 | at most one ARRMS_FORCE_* |
+ *              ARRMS_EXACT_ONLY. ARRMS_FP8 requires bf16 or fp16.
+ * stream       HIP stream; all work is enqueued on it, asynchronously.
+ *
+ * Every device pointer must be 16-byte aligned (fp8_scale: 4-byte aligned).
+ * No output may overlap an input or another output, except residual_out ==
+ * residual. The buffers are caller-owned; the library keeps no reference.
+ * No host synchronisation and no allocation happen on the one-stage path.
+ * The two-stage path uses the library's staging buffer on the current device
+ * (arrms_reserve_staging); outside stream capture it is reserved on first use,
+ * inside capture an unreserved buffer yields ARRMS_ERR_NO_STAGING. Two-stage
+ * calls on one device share that buffer: issue them on one stream, or order
+ * them. The same inputs give the same bits on every call and on both paths.
+ */
+ARRMS_API int arrms_fused(const void *const *rank_in, int R, const void *residual, const void *weight,
+                void *out, void *residual_out, void *fp8_out, float *fp8_scale, int M, int H,
+                float eps, int flags, hipStream_t stream);
+
+/*
+ * arrms_reserve_staging -- allocate the staging buffer of the two-stage path
+ * on the current device, at least `bytes` (0: ARRMS_DEFAULT_STAGING_BYTES), the
+ * per-rank staging region of PR #6699 Changes. A larger existing buffer is
+ * kept. Call it before capturing a graph that may take the two-stage path.
+ * Returns ARRMS_OK or ARRMS_ERR_HIP. Not to be called while work that uses the
+ * buffer is in flight.
+ */
+ARRMS_API int arrms_reserve_staging(size_t bytes);
+
+/* arrms_release_staging -- free the current device's staging buffer (after
+ * synchronising the device). Returns ARRMS_OK or ARRMS_ERR_HIP. */
+ARRMS_API int arrms_release_staging(void);
+
+/* arrms_staging_bytes -- size of the current device's staging buffer (0 if none). */
+ARRMS_API size_t arrms_staging_bytes(void);
+
+/*
+ * arrms_query_path -- which path arrms_fused takes for these sizes and flags
+ * (ARRMS_PATH_*), or a negative status if the arguments are invalid. Pure host
+ * code; touches no device. The choice follows PR #6699 Changes (wide rows
+ * above a size threshold go two-stage, the rest one-stage) with thresholds
+ * measured on MI355X rather than the pages' multi-GPU ones.
+ */
+ARRMS_API int arrms_query_path(int M, int H, int R, int flags);
+
+/* arrms_status_string -- static description of a status code. */
+ARRMS_API const char *arrms_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARRMS_H */

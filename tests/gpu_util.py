@@ -1,0 +1,124 @@
+"""Helpers of the GPU parity tests: run the HIP path and the oracle on the same
+seeded inputs and compare them to the acceptance bars.
+
+Bars (the fused epilogue's definition, restated in include/arrms.h):
+  * residual_out: bit-exact;
+  * out (the T output): within 1 ulp of T (|d| <= 2^-7 |y| bf16, 2^-10 |y| fp16,
+    1 fp32 ulp); the tests also report, and for most cases require, exact bits;
+  * fp8_scale: relative difference <= 1e-6;
+  * fp8_out: >= 99.9 % identical bytes, the rest one code apart (same sign,
+    adjacent magnitudes), and, where the T mirror is written, exactly the
+    per-token quant of the kernel's own mirror and scale.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from all_reduce_residual_rank_amd import arrms
+from all_reduce_residual_rank_amd import workloads as wlmod
+
+TORCH_T = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.float32:
+        return t.numpy().copy()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
+
+
+def poison_(t: torch.Tensor) -> torch.Tensor:
+    """Fill with all-ones bytes (NaN in bf16/fp16/fp32, 0xFF in FP8 codes)."""
+    t.view(torch.uint8).fill_(0xFF)
+    return t
+
+
+def run_hip(wl: wlmod.Workload, xs, res, w, *, flags: int | None = None, mirror: bool | None = None,
+            inplace: bool = False, extra_flags: int = 0):
+    """Run arrms_fused once on device copies of the host inputs; returns host arrays."""
+    dev = torch.device("cuda")
+    T = TORCH_T[wl.dtype]
+    M, H = res.shape
+    flags = (wl.flags if flags is None else flags) | extra_flags
+    mirror = wl.mirror if mirror is None else mirror
+    fp8 = bool(flags & arrms.FP8)
+    xd = [x.to(dev) for x in xs]
+    rd = res.to(dev)
+    wd = w.to(dev)
+    out = poison_(torch.empty(M, H, dtype=T, device=dev)) if (mirror or not fp8) else None
+    rout = rd if inplace else poison_(torch.empty(M, H, dtype=T, device=dev))
+    q = poison_(torch.empty(M, H, dtype=torch.uint8, device=dev)) if fp8 else None
+    sc = poison_(torch.empty(M, dtype=torch.float32, device=dev)) if fp8 else None
+    arrms.arrms_fused(xd, rd, wd, out, rout, q, sc, eps=wl.eps, flags=flags, M=M, H=H)
+    torch.cuda.synchronize()
+    return {"out": None if out is None else host_bits(out), "residual_out": host_bits(rout),
+            "fp8": None if q is None else host_bits(q), "scale": None if sc is None else host_bits(sc)}
+
+
+def run_oracle(wl: wlmod.Workload, xs, res, w, *, flags: int | None = None, mirror: bool | None = None):
+    flags = wl.flags if flags is None else flags
+    mirror = wl.mirror if mirror is None else mirror
+    want_out = mirror or not (flags & oracle.FP8)
+    return oracle.fused([host_bits(x) for x in xs], host_bits(res), host_bits(w), wl.eps,
+                        flags & 0xF, want_out=want_out)
+
+
+def _values(bits: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "fp32":
+        return bits.astype(np.float64)
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return bits.view(np.float16).astype(np.float64)
+
+
+def _ulp_bound(y: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return np.abs(y) * 2.0 ** -7
+    if dtype == "fp16":
+        return np.maximum(np.abs(y) * 2.0 ** -10, 2.0 ** -24)
+    return np.abs(np.spacing(y.astype(np.float32))).astype(np.float64)
+
+
+def _e4m3_mag(codes: np.ndarray) -> np.ndarray:
+    return (codes & 0x7F).astype(np.int64)
+
+
+def compare(got: dict, want: dict, dtype: str, *, require_exact_out: bool = True, label: str = ""):
+    """Assert the acceptance bars; returns a small report dict."""
+    rep = {}
+    assert np.array_equal(got["residual_out"], want["residual_out"]), \
+        f"{label}: residual_out differs in {(got['residual_out'] != want['residual_out']).sum()} elements"
+    if want["out"] is not None:
+        g, w = got["out"], want["out"]
+        same = g == w
+        rep["out_exact_frac"] = float(same.mean())
+        if not same.all():
+            gv, wv = _values(g, dtype), _values(w, dtype)
+            bad = ~same & ~(np.abs(gv - wv) <= _ulp_bound(wv, dtype))
+            assert not bad.any(), f"{label}: {bad.sum()} outputs beyond 1 ulp"
+            assert not require_exact_out, f"{label}: {(~same).sum()} outputs differ by 1 ulp"
+    if want["fp8"] is not None:
+        gs, ws = got["scale"], want["scale"]
+        rel = np.abs(gs.astype(np.float64) - ws) / np.maximum(np.abs(ws.astype(np.float64)), 1e-300)
+        assert np.all((gs == ws) | (rel <= 1e-6)), f"{label}: fp8 scales differ"
+        gq, wq = got["fp8"], want["fp8"]
+        same = gq == wq
+        rep["fp8_exact_frac"] = float(same.mean())
+        assert same.mean() >= 0.999, f"{label}: only {same.mean():.6f} of FP8 bytes identical"
+        diff = ~same
+        if diff.any():
+            zero_pair = ((gq[diff] & 0x7F) == 0) & ((wq[diff] & 0x7F) == 0)
+            one_code = ((gq[diff] & 0x80) == (wq[diff] & 0x80)) & \
+                (np.abs(_e4m3_mag(gq[diff]) - _e4m3_mag(wq[diff])) == 1)
+            assert np.all(zero_pair | one_code), f"{label}: FP8 bytes more than one code apart"
+        if got["out"] is not None:
+            # the pages' identity: FP8 bytes == per-token quant of the kernel's own T mirror
+            dt = 0 if dtype == "bf16" else 1
+            q2, s2 = oracle.quant(got["out"], dt)
+            assert np.array_equal(s2, gs), f"{label}: scale != amax(mirror)/448"
+            assert np.array_equal(q2, gq), f"{label}: FP8 bytes != quant(mirror)"
+    return rep

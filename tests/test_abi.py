@@ -1,0 +1,133 @@
+"""The C ABI on the host (no GPU): the library loads, exports what include/arrms.h
+declares, and rejects bad arguments before touching any device.
+
+Only argument checks are exercised here: every call below returns from the
+host-side validation (or from M == 0) and launches nothing. Device pointers are
+fake, aligned addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from all_reduce_residual_rank_amd import arrms
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "arrms.h")
+
+BASE = 1 << 40          # fake device addresses, far apart
+STRIDE = 1 << 32
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"ARRMS_API\s+[\w\s\*]*?\b(arrms_\w+)\s*\(", text)))
+
+
+def header_constants():
+    text = open(HEADER).read()
+    out = {}
+    for name, val in re.findall(r"#define\s+ARRMS_(\w+)\s+\(?(-?\d+)u?\)?\s", text):
+        out[name] = int(val)
+    return out
+
+
+def test_exports_match_header():
+    decl = declared_functions()
+    assert decl == sorted(arrms.EXPORTS)
+    nm = subprocess.run(["nm", "-D", "--defined-only", arrms.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(arrms_\w+)$", nm, re.M))
+    assert exported == set(decl)
+    lib = ctypes.CDLL(arrms.LIB_PATH)
+    for name in decl:
+        assert getattr(lib, name) is not None
+
+
+def test_binding_constants_match_header():
+    c = header_constants()
+    for name in ("OK", "ERR_INVALID", "ERR_UNSUPPORTED", "ERR_NO_STAGING", "ERR_HIP", "DTYPE_BF16",
+                 "DTYPE_FP16", "DTYPE_FP32", "GEMMA", "FP8", "FORCE_ONE_STAGE", "FORCE_TWO_STAGE",
+                 "EXACT_ONLY", "MAX_RANKS", "MAX_HIDDEN", "PATH_NONE", "PATH_ONE_STAGE",
+                 "PATH_TWO_STAGE"):
+        assert getattr(arrms, name) == c[name], name
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4):
+        assert arrms.arrms_status_string(s) and arrms.arrms_status_string(s) != "unknown status"
+    assert arrms.arrms_status_string(7) == "unknown status"
+
+
+def _call(R=4, M=8, H=64, flags=0, eps=1e-6, **over):
+    ptr = {f"in{r}": BASE + (r if r < 8 else 16) * STRIDE for r in range(9)}
+    ptr.update(residual=BASE + 10 * STRIDE, weight=BASE + 11 * STRIDE, out=BASE + 12 * STRIDE,
+               residual_out=BASE + 13 * STRIDE, fp8_out=BASE + 14 * STRIDE,
+               fp8_scale=BASE + 15 * STRIDE)
+    ptr.update(over)
+    rank_in = [ptr[f"in{r}"] for r in range(R)]
+    return arrms.arrms_fused_raw(rank_in, R, ptr["residual"], ptr["weight"], ptr["out"],
+                                 ptr["residual_out"], ptr["fp8_out"], ptr["fp8_scale"], M, H, eps,
+                                 flags, None)
+
+
+def test_zero_rows_is_ok_and_launches_nothing():
+    assert _call(M=0) == arrms.OK
+    assert arrms.arrms_query_path(0, 6144, 4, 0) == arrms.PATH_NONE
+
+
+@pytest.mark.parametrize("kw", [
+    dict(R=0), dict(R=9), dict(M=-1), dict(H=0), dict(flags=3), dict(flags=1 << 7),
+    dict(flags=arrms.FORCE_ONE_STAGE | arrms.FORCE_TWO_STAGE), dict(eps=-1.0),
+    dict(eps=float("nan")), dict(eps=float("inf")), dict(residual=None), dict(weight=None),
+    dict(residual_out=None), dict(out=None), dict(in2=None),
+    dict(flags=arrms.FP8, fp8_out=None), dict(flags=arrms.FP8, fp8_scale=None),
+])
+def test_invalid_arguments(kw):
+    assert _call(**kw) == arrms.ERR_INVALID
+
+
+@pytest.mark.parametrize("kw", [
+    dict(H=60),                                  # 120 bytes per bf16 row: not 16-byte packs
+    dict(H=6, flags=arrms.DTYPE_FP32),           # 24 bytes per fp32 row
+    dict(H=arrms.MAX_HIDDEN + 8),
+    dict(flags=arrms.DTYPE_FP32 | arrms.FP8),
+    dict(in1=BASE + STRIDE + 8),                 # misaligned rank input
+    dict(residual=BASE + 10 * STRIDE + 2),
+    dict(out=BASE + 12 * STRIDE + 4),
+    dict(flags=arrms.FP8, fp8_scale=BASE + 15 * STRIDE + 2),
+])
+def test_unsupported_layouts(kw):
+    assert _call(**kw) == arrms.ERR_UNSUPPORTED
+
+
+def test_overlap_rules():
+    M, H = 8, 64
+    nbytes = M * H * 2
+    # out overlapping a rank input
+    assert _call(out=BASE + STRIDE + 16) == arrms.ERR_INVALID
+    # residual_out overlapping residual but not equal
+    assert _call(residual_out=BASE + 10 * STRIDE + 16) == arrms.ERR_INVALID
+    # out and residual_out overlapping each other
+    assert _call(out=BASE + 13 * STRIDE + nbytes - 16) == arrms.ERR_INVALID
+    # out overlapping the weight
+    assert _call(out=BASE + 11 * STRIDE) == arrms.ERR_INVALID
+    # fp8 scale inside the fp8 codes
+    assert _call(flags=arrms.FP8, fp8_scale=BASE + 14 * STRIDE + 64) == arrms.ERR_INVALID
+    # adjacent but not overlapping buffers are fine (validation passes; M = 0 stops before launch)
+    assert _call(M=0, out=BASE + 13 * STRIDE + nbytes) == arrms.OK
+    # repeated rank pointers are inputs only: allowed
+    assert _call(M=0, in1=BASE) == arrms.OK
+
+
+def test_query_path():
+    for flags in (0, arrms.DTYPE_FP16, arrms.DTYPE_FP16 | arrms.GEMMA | arrms.FP8):
+        assert arrms.arrms_query_path(1024, 6144, 4, flags) in (arrms.PATH_ONE_STAGE,
+                                                                arrms.PATH_TWO_STAGE)
+    assert arrms.arrms_query_path(1024, 6144, 4, arrms.FORCE_TWO_STAGE) == arrms.PATH_TWO_STAGE
+    assert arrms.arrms_query_path(1024, 6144, 4, arrms.FORCE_ONE_STAGE) == arrms.PATH_ONE_STAGE
+    assert arrms.arrms_query_path(1024, 60, 4, 0) == arrms.ERR_UNSUPPORTED
+    assert arrms.arrms_query_path(1024, 64, 9, 0) == arrms.ERR_INVALID
+    assert arrms.arrms_query_path(16, 512, 4, arrms.DTYPE_FP32 | arrms.FP8) == arrms.ERR_UNSUPPORTED

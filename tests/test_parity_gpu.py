@@ -1,0 +1,272 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on a GPU.
+
+Every case runs the oracle and the HIP kernels on the same seeded host inputs
+and compares them element by element over the whole output (the oracle is
+plain C and finishes even the 2800 x 6144 and 2048 x 7168 x R=8 workloads in
+seconds). Outputs are poisoned with NaN bytes before each call so that an
+element the kernels fail to write shows up.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from all_reduce_residual_rank_amd import workloads as wlmod
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from all_reduce_residual_rank_amd import arrms
+else:  # pragma: no cover - collected on CPU only with -m gpu deselected
+    arrms = None
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_shapes.json")
+PATHS = {"one": 16, "two": 32}   # FORCE_ONE_STAGE / FORCE_TWO_STAGE
+
+
+def _case(wl, seed, paths, **kw):
+    """Oracle once, then the HIP path once per named path; all compared to the oracle."""
+    if isinstance(paths, str):
+        paths = (paths,)
+    xs, res, w = wlmod.make_inputs(wl, seed=seed)
+    want = gu.run_oracle(wl, xs, res, w)
+    for path in paths:
+        print(f"case {wl.name} R={wl.R} M={wl.M} H={wl.H} {wl.dtype} flags={wl.flags} "
+              f"seed={seed} path={path}", flush=True)
+        got = gu.run_hip(wl, xs, res, w, extra_flags=PATHS[path], **kw)
+        gu.compare(got, want, wl.dtype, label=f"{wl.name}/s{seed}/{path}")
+
+
+@pytest.mark.parametrize("path", ["one", "two"])
+@pytest.mark.parametrize("wl", wlmod.ALL, ids=lambda w: w.name)
+def test_workloads_seed0(wl, path):
+    _case(wl, 0, path)
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3, 4])
+@pytest.mark.parametrize("wl", wlmod.ALL, ids=lambda w: w.name)
+def test_workloads_more_seeds(wl, seed):
+    _case(wl, seed, "one")
+
+
+def test_fp8_with_mirror_matches_quant_of_mirror():
+    _case(wlmod.FP8_GEMMA.with_(mirror=True), 0, ("one", "two"))
+
+
+@pytest.mark.parametrize("wl", [wlmod.HEADLINE, wlmod.FP8_GEMMA.with_(mirror=True), wlmod.TAIL_FP32,
+                                wlmod.TAILS[2]], ids=lambda w: w.name)
+def test_fast_branches_equal_exact_branches(wl):
+    xs, res, w = wlmod.make_inputs(wl, seed=7)
+    fast = gu.run_hip(wl, xs, res, w)
+    exact = gu.run_hip(wl, xs, res, w, extra_flags=arrms.EXACT_ONLY)
+    for k in fast:
+        if fast[k] is not None:
+            assert np.array_equal(fast[k], exact[k]), k
+
+
+@pytest.mark.parametrize("wl", [wlmod.SMALL, wlmod.HEADLINE, wlmod.FP8_GEMMA.with_(mirror=True),
+                                wlmod.WIDE_R8, wlmod.TAIL_FP32] + wlmod.TAILS,
+                         ids=lambda w: w.name)
+def test_one_stage_equals_two_stage_bitwise(wl):
+    xs, res, w = wlmod.make_inputs(wl, seed=3)
+    a = gu.run_hip(wl, xs, res, w, extra_flags=PATHS["one"])
+    b = gu.run_hip(wl, xs, res, w, extra_flags=PATHS["two"])
+    for k in a:
+        if a[k] is not None:
+            assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("path", ["one", "two"])
+def test_inplace_residual(path):
+    wl = wlmod.TAILS[4]
+    xs, res, w = wlmod.make_inputs(wl, seed=1)
+    want = gu.run_oracle(wl, xs, res, w)
+    got = gu.run_hip(wl, xs, res, w, inplace=True, extra_flags=PATHS[path])
+    gu.compare(got, want, wl.dtype, label="inplace")
+
+
+def _page_shape_cases():
+    g = json.load(open(GOLDEN))
+    cases = []
+    for M, H in g["fused_kernel_check_tp4"]["rows_hidden"]:
+        cases.append(("tp4", 4, M, H))
+    for M, H in g["fused_kernel_check_tp2"]["rows_hidden"]:
+        cases.append(("tp2", 2, M, H))
+    for M, H in g["fp8_identity"]["rows_hidden"]:
+        cases.append(("fp8", 4, M, H))
+    for M in g["upstream_2880"]["rows"]:
+        cases.append(("up2880", 4, M, 2880))
+    for M in g["decode_m"]["rows"]:
+        cases.append(("decode", 8, M, 6144))
+    return cases
+
+
+@pytest.mark.parametrize("case", _page_shape_cases(), ids=lambda c: f"{c[0]}-R{c[1]}-{c[2]}x{c[3]}")
+def test_page_shapes(case):
+    kind, R, M, H = case
+    variants = [dict(dtype="bf16"), dict(dtype="fp16", gemma=True, w_mean=0.0)]
+    if kind == "fp8":
+        variants = [dict(dtype="bf16", fp8=True, mirror=True),
+                    dict(dtype="fp16", fp8=True, mirror=True, gemma=True, w_mean=0.0)]
+    for v in variants:
+        _case(wlmod.Workload(f"{kind}", R=R, M=M, H=H, **v), 11, ("one", "two"))
+
+
+@pytest.mark.parametrize("R", range(1, 9))
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_every_rank_count(R, dtype):
+    wl = wlmod.Workload("rsweep", R=R, M=37, H=1024 if dtype != "fp32" else 512, dtype=dtype,
+                        fp8=dtype != "fp32", mirror=True, row_scale=(0.1, 10.0))
+    _case(wl, R, ("one", "two"))
+
+
+@pytest.mark.parametrize("H", [8, 16, 64, 136, 504, 520, 1016, 3072, 5120, 8200, 16384])
+def test_hidden_sizes_and_tails(H):
+    wl = wlmod.Workload("hsweep", R=3, M=19, H=H, dtype="bf16", fp8=True, mirror=True)
+    _case(wl, 5, ("one", "two"))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_exact_integer_sums(dtype):
+    # the exact-integer generator of PR #5807's reproducer at its tail neighbours
+    for M in (1023, 1024, 1025):
+        H = 512
+        xs = wlmod.exact_integer_inputs(4, M, H, seed=100 + M, dtype=dtype)
+        wl = wlmod.Workload("exint", R=4, M=M, H=H, dtype=dtype)
+        res = torch.zeros(M, H, dtype=gu.TORCH_T[dtype])
+        w = torch.ones(H, dtype=gu.TORCH_T[dtype])
+        want = gu.run_oracle(wl, xs, res, w)
+        idx = np.arange(M * H).reshape(M, H)
+        exact = sum(((idx * (r + 1) + (100 + M) * (r + 3)) % 31) - 15 for r in range(4))
+        for path in ("one", "two"):
+            got = gu.run_hip(wl, xs, res, w, extra_flags=PATHS[path])
+            gu.compare(got, want, dtype, label=f"exint{M}")
+            assert np.array_equal(gu._values(got["residual_out"], dtype), exact.astype(np.float64))
+
+
+def test_special_values():
+    # zero rows (FP8 scale 0, signed zeros), a row spanning a wide dynamic range
+    # (FP8 subnormal codes, fp16 subnormal outputs), and a row hitting saturation.
+    M, H = 6, 1024
+    for dtype in ("bf16", "fp16"):
+        T = gu.TORCH_T[dtype]
+        g = torch.Generator().manual_seed(0)
+        base = torch.randn(M, H, generator=g)
+        x0 = base.clone()
+        x0[0] = -0.0
+        x0[1] = 0.0
+        x0[2] = base[2] * torch.logspace(-7, 3, H)
+        x0[3, :] = 1e-3
+        x0[3, 17] = 3e4 if dtype == "fp16" else 3e30
+        xs = [x0.to(T)] + [torch.zeros(M, H).to(T) for _ in range(2)]
+        xs[1][0] = -0.0
+        xs[2][0] = -0.0
+        res = torch.zeros(M, H).to(T)
+        res[0] = -0.0
+        w = (torch.randn(H, generator=g) * 0.1 + 1.0).to(T)
+        wl = wlmod.Workload("special", R=3, M=M, H=H, dtype=dtype, fp8=True, mirror=True)
+        want = gu.run_oracle(wl, xs, res, w)
+        assert want["scale"][0] == 0 and want["scale"][1] == 0
+        for path in ("one", "two"):
+            for extra in (0, arrms.EXACT_ONLY):
+                got = gu.run_hip(wl, xs, res, w, extra_flags=PATHS[path] | extra)
+                gu.compare(got, want, dtype, label=f"special-{dtype}-{path}")
+                assert np.array_equal(got["fp8"], want["fp8"])
+
+
+def test_deterministic_repeat():
+    wl = wlmod.HEADLINE
+    xs, res, w = wlmod.make_inputs(wl, seed=0)
+    a = gu.run_hip(wl, xs, res, w)
+    b = gu.run_hip(wl, xs, res, w)
+    for k in a:
+        if a[k] is not None:
+            assert np.array_equal(a[k], b[k])
+
+
+def test_graph_replay_with_changing_inputs():
+    # Capture one call per path in a HIP graph, then replay with new inputs copied
+    # into the captured buffers and NaN-poisoned outputs, checking every replay.
+    dev = torch.device("cuda")
+    wl = wlmod.Workload("graph", R=4, M=300, H=2880, dtype="fp16", gemma=True, fp8=True, mirror=True,
+                        w_mean=0.0)
+    arrms.arrms_reserve_staging(0)
+    xs0, res0, w0 = wlmod.make_inputs(wl, seed=0)
+    xd = [x.to(dev) for x in xs0]
+    rd, wd = res0.to(dev), w0.to(dev)
+    outs = {}
+    graphs = {}
+    for path in ("one", "two"):
+        o = {"out": torch.empty(wl.M, wl.H, dtype=torch.float16, device=dev),
+             "rout": torch.empty(wl.M, wl.H, dtype=torch.float16, device=dev),
+             "q": torch.empty(wl.M, wl.H, dtype=torch.uint8, device=dev),
+             "sc": torch.empty(wl.M, dtype=torch.float32, device=dev)}
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            arrms.arrms_fused(xd, rd, wd, o["out"], o["rout"], o["q"], o["sc"], eps=wl.eps,
+                              flags=wl.flags | PATHS[path], stream=s)
+        torch.cuda.current_stream().wait_stream(s)
+        outs[path], graphs[path] = o, g
+    for step in range(3):
+        xs, res, w = wlmod.make_inputs(wl, seed=10 + step)
+        for d, h in zip(xd, xs):
+            d.copy_(h)
+        rd.copy_(res)
+        wd.copy_(w)
+        want = gu.run_oracle(wl, xs, res, w)
+        for path in ("one", "two"):
+            o = outs[path]
+            for t in o.values():
+                gu.poison_(t)
+            torch.cuda.synchronize()
+            graphs[path].replay()
+            torch.cuda.synchronize()
+            got = {"out": gu.host_bits(o["out"]), "residual_out": gu.host_bits(o["rout"]),
+                   "fp8": gu.host_bits(o["q"]), "scale": gu.host_bits(o["sc"])}
+            gu.compare(got, want, "fp16", label=f"graph-{path}-{step}")
+
+
+def test_two_stage_in_capture_without_staging_is_refused():
+    dev = torch.device("cuda")
+    torch.cuda.synchronize()
+    arrms.arrms_release_staging()
+    assert arrms.arrms_staging_bytes() == 0
+    M, H = 8, 512
+    xs = [torch.randn(M, H, device=dev).to(torch.bfloat16) for _ in range(2)]
+    res = torch.randn(M, H, device=dev).to(torch.bfloat16)
+    w = torch.ones(H, device=dev, dtype=torch.bfloat16)
+    out = torch.empty_like(res)
+    rout = torch.empty_like(res)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    dummy = torch.zeros(1, device=dev)
+    with torch.cuda.graph(g, stream=s):
+        dummy.add_(1)
+        rc = arrms.arrms_fused_raw(xs, 2, res, w, out, rout, None, None, M, H, 1e-6,
+                                   arrms.FORCE_TWO_STAGE, s.cuda_stream)
+    assert rc == arrms.ERR_NO_STAGING
+    # outside capture the same call reserves staging lazily and succeeds
+    rc = arrms.arrms_fused_raw(xs, 2, res, w, out, rout, None, None, M, H, 1e-6,
+                               arrms.FORCE_TWO_STAGE, torch.cuda.current_stream().cuda_stream)
+    assert rc == arrms.OK
+    torch.cuda.synchronize()
+    assert arrms.arrms_staging_bytes() == arrms.DEFAULT_STAGING_BYTES
+
+
+def test_small_staging_forces_many_chunks():
+    # a staging buffer of a few rows exercises the chunk loop (and its row offsets)
+    torch.cuda.synchronize()
+    arrms.arrms_release_staging()
+    arrms.arrms_reserve_staging(7 * 2880 * 2 + 100)
+    wl = wlmod.Workload("chunks", R=4, M=121, H=2880, dtype="fp16", fp8=True, mirror=True)
+    try:
+        _case(wl, 2, "two")
+    finally:
+        torch.cuda.synchronize()
+        arrms.arrms_release_staging()
