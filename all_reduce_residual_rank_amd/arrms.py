@@ -43,12 +43,15 @@ MAX_HIDDEN = 16384
 DEFAULT_STAGING_BYTES = 16 << 20
 PATH_NONE, PATH_ONE_STAGE, PATH_TWO_STAGE = 0, 1, 2
 
-EXPORTS = ("arrms_fused", "arrms_reserve_staging", "arrms_release_staging",
+EXPORTS = ("arrms_fused", "arrms_fused_config", "arrms_reserve_staging", "arrms_release_staging",
            "arrms_staging_bytes", "arrms_query_path", "arrms_status_string")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _lib.arrms_fused.argtypes = [ctypes.POINTER(_vp), _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _vp]
 _lib.arrms_fused.restype = _i
+_lib.arrms_fused_config.argtypes = [ctypes.POINTER(_vp), _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i,
+                                    _i, _i, _i, _vp]
+_lib.arrms_fused_config.restype = _i
 _lib.arrms_reserve_staging.argtypes = [_sz]
 _lib.arrms_reserve_staging.restype = _i
 _lib.arrms_release_staging.argtypes = []
@@ -97,6 +100,29 @@ def arrms_fused_raw(rank_in, R, residual, weight, out, residual_out, fp8_out, fp
     return _lib.arrms_fused(ptrs, int(R), _addr(residual), _addr(weight), _addr(out),
                             _addr(residual_out), _addr(fp8_out), _addr(fp8_scale), int(M), int(H),
                             float(eps), int(flags), stream)
+
+
+def arrms_fused_config_raw(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale,
+                           M, H, eps, flags, ppt, tpr, rows_per_block, stream) -> int:
+    """arrms_fused_config with addresses as ints; returns the status unchanged."""
+    ptrs = (_vp * max(len(rank_in), 1))(*[_addr(p) for p in rank_in])
+    return _lib.arrms_fused_config(ptrs, int(R), _addr(residual), _addr(weight), _addr(out),
+                                   _addr(residual_out), _addr(fp8_out), _addr(fp8_scale), int(M),
+                                   int(H), float(eps), int(flags), int(ppt), int(tpr),
+                                   int(rows_per_block), stream)
+
+
+def arrms_fused_config(rank_in, residual, weight, out, residual_out, fp8_out=None, fp8_scale=None, *,
+                       eps: float, flags: int, ppt: int = 0, tpr: int = 0, rows_per_block: int = 0,
+                       M: int | None = None, H: int | None = None, stream=None) -> None:
+    """arrms_fused with an explicit row-kernel launch shape (0 = automatic)."""
+    if M is None or H is None:
+        M, H = residual.shape[-2], residual.shape[-1]
+    rc = arrms_fused_config_raw(rank_in, len(rank_in), residual, weight, out, residual_out, fp8_out,
+                                fp8_scale, M, H, eps, flags, ppt, tpr, rows_per_block,
+                                _stream_handle(stream))
+    if rc != OK:
+        raise ArrmsError(rc, "arrms_fused_config")
 
 
 def arrms_fused(rank_in, residual, weight, out, residual_out, fp8_out=None, fp8_scale=None, *,

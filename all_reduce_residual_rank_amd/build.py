@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libarrms.so")
 
-SOURCES = ["kern_bf16.hip", "kern_fp16.hip", "kern_fp32.hip", "api.cpp"]
+SOURCES = ["kern_bf16_t.hip", "kern_bf16_fp8.hip", "kern_bf16_fp8t.hip", "kern_fp16_t.hip",
+           "kern_fp16_fp8.hip", "kern_fp16_fp8t.hip", "kern_fp32_t.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: keep the compiler from forming packed fp32 arithmetic;

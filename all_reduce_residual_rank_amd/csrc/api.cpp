@@ -146,49 +146,61 @@ int choose_path(int M, int H, int R, int flags)
     return ARRMS_PATH_ONE_STAGE;
 }
 
-// Row-kernel shape for P packs per row: PPT in {1,2,4,8} (bounded by the
-// register budget for R+1 streams), tpr = PPT-covering multiple of 64 up to
-// 512. Prefer an exact cover (no tail), then the least padding, then tpr
-// nearest 256.
+// Row-kernel shape for P packs per row: PPT in {1,2,4}, tpr = the PPT-covering
+// multiple of 64 up to 512. Prefer an exact cover (no idle lanes), then the
+// least padding, then more packs per thread (fewer, busier threads: measured
+// faster on MI355X) as long as a thread's R+1 input packs stay within 20
+// (80 registers), which keeps several blocks resident per compute unit.
 arrms::RowShape choose_shape(int P, int R, long long M)
 {
-    arrms::RowShape best = {0, 0, 0, false, 0};
+    (void)M;
+    arrms::RowShape best = {0, 0, 0, false};
     long long best_key = -1;
-    const int ppts[4] = {1, 2, 4, 8};
-    for (int c = 0; c < 4; ++c) {
+    const int ppts[3] = {1, 2, 4};
+    for (int c = 0; c < 3; ++c) {
         const int ppt = ppts[c];
-        if (ppt * (R + 1) > 45)
+        if (ppt > 1 && ppt * (R + 1) > 20)
             continue;
         int tpr = (P + ppt - 1) / ppt;
         tpr = (tpr + 63) / 64 * 64;
         if (tpr > 512)
             continue;
         const int waste = tpr * ppt - P;
-        const int dist = tpr > 256 ? tpr - 256 : 256 - tpr;
-        const long long key = (long long)waste * 4096 + dist;
+        const long long key = (long long)waste * 16 + (4 - ppt);
         if (best_key < 0 || key < best_key) {
             best_key = key;
-            best = {ppt, tpr, 1, waste != 0, 0};
+            best = {ppt, tpr, 1, waste != 0};
+        }
+    }
+    if (best.ppt == 0) {
+        // wide rows with many ranks: the register budget gives way to coverage
+        for (int c = 0; c < 3 && best.ppt == 0; ++c) {
+            int tpr = (P + ppts[c] - 1) / ppts[c];
+            tpr = (tpr + 63) / 64 * 64;
+            if (tpr <= 512)
+                best = {ppts[c], tpr, 1, tpr * ppts[c] != P};
         }
     }
     if (best.ppt == 0)
         return best;
     best.rpb = best.tpr >= 256 ? 1 : 256 / best.tpr;
-    const long long groups = (M + best.rpb - 1) / best.rpb;
-    const long long cap = 256LL * 32;  // grid-stride beyond this
-    best.grid = (int)(groups < cap ? groups : cap);
-    if (best.grid < 1)
-        best.grid = 1;
     return best;
 }
 
-hipError_t launch_row(int dt, const arrms::RowArgs &a, int R, const arrms::RowShape &s,
-                      hipStream_t st)
+hipError_t launch_row(int dt, bool fp8, bool mirror, const arrms::RowArgs &a, int R,
+                      const arrms::RowShape &s, hipStream_t st)
 {
     switch (dt) {
-    case DT_BF16: return arrms::launch_row_bf16(a, R, s, st);
-    case DT_FP16: return arrms::launch_row_fp16(a, R, s, st);
-    default: return arrms::launch_row_fp32(a, R, s, st);
+    case DT_BF16:
+        if (!fp8)
+            return arrms::launch_row_bf16_t(a, R, s, st);
+        return mirror ? arrms::launch_row_bf16_fp8t(a, R, s, st) : arrms::launch_row_bf16_fp8(a, R, s, st);
+    case DT_FP16:
+        if (!fp8)
+            return arrms::launch_row_fp16_t(a, R, s, st);
+        return mirror ? arrms::launch_row_fp16_fp8t(a, R, s, st) : arrms::launch_row_fp16_fp8(a, R, s, st);
+    default:
+        return arrms::launch_row_fp32_t(a, R, s, st);
     }
 }
 
@@ -305,9 +317,46 @@ size_t arrms_staging_bytes(void)
     return g_staging[dev].ptr ? g_staging[dev].bytes : 0;
 }
 
-int arrms_fused(const void *const *rank_in, int R, const void *residual, const void *weight,
-                void *out, void *residual_out, void *fp8_out, float *fp8_scale, int M, int H,
-                float eps, int flags, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+struct ShapeReq {
+    int ppt, tpr, rpb;  // 0 = automatic
+};
+
+// Apply an explicit shape request on top of the automatic choice; returns
+// false when the request cannot cover a row of P packs.
+bool apply_shape(const ShapeReq *req, int P, int R, long long M, arrms::RowShape &s)
+{
+    (void)R;
+    (void)M;
+    if (!req)
+        return true;
+    if (req->ppt) {
+        if (req->ppt != 1 && req->ppt != 2 && req->ppt != 4)
+            return false;
+        s.ppt = req->ppt;
+        int tpr = (P + s.ppt - 1) / s.ppt;
+        s.tpr = (tpr + 63) / 64 * 64;
+    }
+    if (req->tpr) {
+        if (req->tpr % 64)
+            return false;
+        s.tpr = req->tpr;
+    }
+    if ((long long)s.tpr * s.ppt < P || s.tpr > 512)
+        return false;
+    s.tail = s.tpr * s.ppt != P;
+    s.rpb = req->rpb ? req->rpb : (s.tpr >= 256 ? 1 : 256 / s.tpr);
+    if (s.rpb < 1 || s.tpr * s.rpb > 512)
+        return false;
+    return true;
+}
+
+int fused_impl(const void *const *rank_in, int R, const void *residual, const void *weight,
+               void *out, void *residual_out, void *fp8_out, float *fp8_scale, int M, int H,
+               float eps, int flags, const ShapeReq *req, hipStream_t stream)
 {
     int rc = validate(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H,
                       eps, flags);
@@ -334,7 +383,6 @@ int arrms_fused(const void *const *rank_in, int R, const void *residual, const v
     a.H = H;
     a.eps = eps;
     a.gemma = (flags & ARRMS_GEMMA) != 0;
-    a.fp8 = fp8;
     a.exact_only = (flags & ARRMS_EXACT_ONLY) != 0;
 
     (void)hipGetLastError();  // launches below report their own errors
@@ -343,10 +391,10 @@ int arrms_fused(const void *const *rank_in, int R, const void *residual, const v
             a.in[r] = rank_in[r];
         a.M = M;
         arrms::RowShape s = choose_shape(P, R, M);
-        if (s.ppt == 0)
+        if (s.ppt == 0 || !apply_shape(req, P, R, M, s))
             return ARRMS_ERR_UNSUPPORTED;
         a.tpr = s.tpr;
-        return launch_row(dt, a, R, s, stream) == hipSuccess ? ARRMS_OK : ARRMS_ERR_HIP;
+        return launch_row(dt, fp8, out != nullptr, a, R, s, stream) == hipSuccess ? ARRMS_OK : ARRMS_ERR_HIP;
     }
 
     // ---- two-stage: per row chunk, flat rank reduce into staging, then the
@@ -401,14 +449,38 @@ int arrms_fused(const void *const *rank_in, int R, const void *residual, const v
         b.M = n;
         // the row pass takes the one-stage shape of these rows, so both paths
         // reduce the row statistics in the same order and give the same bits
-        const arrms::RowShape s = choose_shape(P, R, n);
-        if (s.ppt == 0)
+        arrms::RowShape s = choose_shape(P, R, n);
+        if (s.ppt == 0 || !apply_shape(req, P, R, n, s))
             return ARRMS_ERR_UNSUPPORTED;
         b.tpr = s.tpr;
-        if (launch_row(dt, b, 1, s, stream) != hipSuccess)
+        if (launch_row(dt, fp8, out != nullptr, b, 1, s, stream) != hipSuccess)
             return ARRMS_ERR_HIP;
     }
     return ARRMS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int arrms_fused(const void *const *rank_in, int R, const void *residual, const void *weight,
+                void *out, void *residual_out, void *fp8_out, float *fp8_scale, int M, int H,
+                float eps, int flags, hipStream_t stream)
+{
+    return fused_impl(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H, eps,
+                      flags, nullptr, stream);
+}
+
+int arrms_fused_config(const void *const *rank_in, int R, const void *residual, const void *weight,
+                       void *out, void *residual_out, void *fp8_out, float *fp8_scale, int M, int H,
+                       float eps, int flags, int ppt, int tpr, int rows_per_block,
+                       hipStream_t stream)
+{
+    if (ppt < 0 || tpr < 0 || rows_per_block < 0)
+        return ARRMS_ERR_INVALID;
+    const ShapeReq req = {ppt, tpr, rows_per_block};
+    return fused_impl(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H, eps,
+                      flags, &req, stream);
 }
 
 }  // extern "C"

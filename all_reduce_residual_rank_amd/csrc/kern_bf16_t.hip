@@ -1,0 +1,16 @@
+// kern_bf16_t.hip -- row kernels for T = bf16 with the T output, and the flat rank reduce.
+#include "kernels.hpp"
+
+namespace arrms {
+
+hipError_t launch_row_bf16_t(const RowArgs &a, int R, const RowShape &s, hipStream_t st)
+{
+    return row_launch_epi<DT_BF16, EPI_T>(a, R, s, st);
+}
+
+hipError_t launch_flat_bf16(const FlatArgs &a, int R, hipStream_t st)
+{
+    return flat_launch<DT_BF16>(a, R, st);
+}
+
+}  // namespace arrms

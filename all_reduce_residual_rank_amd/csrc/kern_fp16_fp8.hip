@@ -1,0 +1,11 @@
+// kern_fp16_fp8.hip -- row kernels for T = fp16 with the FP8 output (no T mirror).
+#include "kernels.hpp"
+
+namespace arrms {
+
+hipError_t launch_row_fp16_fp8(const RowArgs &a, int R, const RowShape &s, hipStream_t st)
+{
+    return row_launch_epi<DT_FP16, EPI_FP8>(a, R, s, st);
+}
+
+}  // namespace arrms

@@ -188,230 +188,315 @@ ARRMS_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" 
 
 ARRMS_DEV u32x4 ld16(const void *p, long long i) { return ((const u32x4 *)p)[i]; }
 ARRMS_DEV void st16(void *p, long long i, u32x4 v) { ((u32x4 *)p)[i] = v; }
+// Streaming (read-once / write-once) data: non-temporal accesses, so the rank
+// inputs and the outputs do not displace the reused lines (weights) in the
+// caches.
+ARRMS_DEV u32x4 ld16_nt(const void *p, long long i)
+{
+    return __builtin_nontemporal_load((const u32x4 *)p + i);
+}
+ARRMS_DEV void st16_nt(void *p, long long i, u32x4 v) { __builtin_nontemporal_store(v, (u32x4 *)p + i); }
 
 // --------------------------------------------------------------------------
 // Row kernel. A block holds rpb row groups of tpr threads (tpr a multiple of
-// 64); a row group owns one row at a time and each of its threads owns PPT
-// packs of it (pack j = lane_in_group + k * tpr). Rows are visited with a
-// grid stride; every thread runs the same number of loop trips and barriers
-// (rows past M run as idle slots), so no barrier sits in divergent control
-// flow (PR #5807 Proposed modifications). TAIL=false is the aligned variant
-// (tpr * PPT == packs per row): no predicates at all.
-template <int DT, int R, int PPT, bool TAIL>
-__global__ void __launch_bounds__(512) row_kernel(const RowArgs a)
+// 64); a row group owns one row and each of its threads owns PPT packs of it
+// (pack j = lane_in_group + k * tpr). The grid has one block per row group, so
+// all rows the device can hold are in flight at once and a finished block is
+// replaced at once by the dispatcher; a lean register budget (the row's R+1
+// input packs, its h values and its weights) keeps several blocks resident
+// per compute unit. Every thread of a block runs the same barriers (rows past
+// M are idle slots), so no barrier sits in divergent control flow (PR #5807
+// Proposed modifications). A ragged row (tpr * PPT > packs per row) needs no
+// separate variant: the buffer range check zero-fills the missing packs and
+// drops their stores, and zeros add nothing to the sum of squares or the
+// maximum. EPI selects the epilogue: T output only, FP8 only, or FP8 with the
+// T mirror.
+enum Epilogue { EPI_T = 0, EPI_FP8 = 1, EPI_FP8_T = 2 };
+
+template <int R, int PPT> struct RowBuf {
+    u32x4 x[R][PPT];
+    u32x4 res[PPT];
+};
+
+struct RowCtx {
+    int lt;      // thread index within the row group
+    int tpr;     // threads per row group
+    int P;       // packs per row
+    int slot;    // row group index within the block
+    int wave;    // wave index within the block
+    int lane;
+    int wpr;     // waves per row group
+    int rpb;     // row groups per block
+};
+
+// Memory access of the row kernel: buffer instructions. A row's base address
+// is wave-uniform, so each stream gets a buffer resource (4 scalar registers)
+// covering exactly that row, and a lane adds its 32-bit byte offset: one
+// offset register serves every stream. The hardware range check of the
+// resource does the tail handling: a load past the row returns zero and a
+// store past it is dropped, so ragged rows run the same instruction stream as
+// aligned ones, with no predicates and no divergent barriers.
+constexpr int kBufAuxNT = 2;               // cache policy: non-temporal
+constexpr int kBufDword3 = 0x00020000;     // 32-bit data format, raw (untyped) access
+
+ARRMS_DEV __amdgpu_buffer_rsrc_t row_rsrc(const void *base, long long row, int row_bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)base + row * (long long)row_bytes),
+                                             (short)0, row_bytes, kBufDword3);
+}
+
+ARRMS_DEV u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kBufAuxNT));
+}
+
+ARRMS_DEV void bstore(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kBufAuxNT);
+}
+
+ARRMS_DEV void bstore8(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kBufAuxNT);
+}
+
+template <int R, int PPT>
+ARRMS_DEV void load_rows(const RowArgs &a, const RowCtx &c, long long g, RowBuf<R, PPT> &b)
+{
+    const long long row = g * c.rpb + c.slot;
+    if (row >= a.M)
+        return;
+    const int rb = c.P * 16;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.in[r], row, rb);
+#pragma unroll
+        for (int k = 0; k < PPT; ++k)
+            b.x[r][k] = bload(rs, (uint32_t)(c.lt + k * c.tpr) * 16u);
+    }
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.residual, row, rb);
+#pragma unroll
+    for (int k = 0; k < PPT; ++k)
+        b.res[k] = bload(rs, (uint32_t)(c.lt + k * c.tpr) * 16u);
+}
+
+template <int DT, int R, int PPT, int EPI>
+ARRMS_DEV void process_rows(const RowArgs &a, const RowCtx &c, long long g, const RowBuf<R, PPT> &b,
+                            const u32x4 (&wv)[PPT], double (&red)[2][kMaxWavesPerBlock][2],
+                            int &parity)
 {
     using F = Fmt<DT>;
     constexpr int EPW = F::EPW;
-    const int tid = threadIdx.x;
-    const int tpr = a.tpr;
-    const int wpr = tpr >> 6;
-    const int rpb = (int)blockDim.x / tpr;
-    const int slot = tid / tpr;
-    const int lt = tid - slot * tpr;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int P = a.P;
+    constexpr bool FP8 = (EPI != EPI_T);
+    constexpr bool OUT_T = (EPI != EPI_FP8);
     const bool gemma = a.gemma != 0;
-    const bool fp8 = (DT != DT_FP32) && a.fp8 != 0;
     const bool exact_only = a.exact_only != 0;
+    const long long row = g * c.rpb + c.slot;
+    const bool valid = row < a.M;
+    const int rb = c.P * 16;
 
-    __shared__ double red[2][kMaxWavesPerBlock][2];
-
-    u32x4 wv[PPT];
+    // ---- rank sum, residual add, sum of squares (and max |h * w_eff|)
+    u32x4 hv[PPT];
+    double ss = 0.0;
+    double pm = 0.0;
+    if (valid) {
+        const __amdgpu_buffer_rsrc_t rout = row_rsrc(a.residual_out, row, rb);
 #pragma unroll
-    for (int k = 0; k < PPT; ++k) {
-        const int j = lt + k * tpr;
-        wv[k] = (!TAIL || j < P) ? ld16(a.weight, j) : u32x4{0u, 0u, 0u, 0u};
-    }
-
-    const long long groups = (a.M + rpb - 1) / rpb;
-    int parity = 0;
-    for (long long g = blockIdx.x; g < groups; g += gridDim.x) {
-        const long long row = g * rpb + slot;
-        const bool valid = row < a.M;
-        const long long base = row * (long long)P;
-
-        // ---- loads: all R inputs and the residual for this thread's packs
-        u32x4 xv[R][PPT];
-        u32x4 rv[PPT];
-        if (valid) {
+        for (int k = 0; k < PPT; ++k) {
 #pragma unroll
-            for (int k = 0; k < PPT; ++k) {
-                const int j = lt + k * tpr;
-                if (!TAIL || j < P) {
+            for (int i = 0; i < 4; ++i) {
+                float acc[EPW];
+                F::unpack(b.x[0][k][i], acc);
 #pragma unroll
-                    for (int r = 0; r < R; ++r)
-                        xv[r][k] = ld16(a.in[r], base + j);
-                    rv[k] = ld16(a.residual, base + j);
+                for (int r = 1; r < R; ++r) {
+                    float t[EPW];
+                    F::unpack(b.x[r][k][i], t);
+#pragma unroll
+                    for (int e = 0; e < EPW; ++e)
+                        acc[e] = acc[e] + t[e];
                 }
-            }
-        }
-
-        // ---- rank sum, residual add, sum of squares (and max |h * w_eff|)
-        u32x4 hv[PPT];
-        double ss = 0.0;
-        double pm = 0.0;
-        if (valid) {
+                float av[EPW], rs[EPW], hf[EPW];
+                F::unpack(F::pack(acc), av);  // a = RNE_T(sum)
+                F::unpack(b.res[k][i], rs);
 #pragma unroll
-            for (int k = 0; k < PPT; ++k) {
-                const int j = lt + k * tpr;
-                if (!TAIL || j < P) {
+                for (int e = 0; e < EPW; ++e)
+                    acc[e] = av[e] + rs[e];
+                const uint32_t hw = F::pack(acc);  // h = RNE_T(a + res)
+                hv[k][i] = hw;
+                F::unpack(hw, hf);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float acc[EPW];
-                        F::unpack(xv[0][k][i], acc);
-#pragma unroll
-                        for (int r = 1; r < R; ++r) {
-                            float t[EPW];
-                            F::unpack(xv[r][k][i], t);
-#pragma unroll
-                            for (int e = 0; e < EPW; ++e)
-                                acc[e] = acc[e] + t[e];
-                        }
-                        float av[EPW], rs[EPW], hf[EPW];
-                        F::unpack(F::pack(acc), av);  // a = RNE_T(sum)
-                        F::unpack(rv[k][i], rs);
-#pragma unroll
-                        for (int e = 0; e < EPW; ++e)
-                            acc[e] = av[e] + rs[e];
-                        const uint32_t hw = F::pack(acc);  // h = RNE_T(a + res)
-                        hv[k][i] = hw;
-                        F::unpack(hw, hf);
-#pragma unroll
-                        for (int e = 0; e < EPW; ++e) {
-                            const double hd = (double)hf[e];
-                            ss = __builtin_fma(hd, hd, ss);  // h^2 is exact in fp64
-                        }
-                        if (fp8) {
-                            float wf[EPW];
-                            F::unpack(wv[k][i], wf);
-#pragma unroll
-                            for (int e = 0; e < EPW; ++e) {
-                                const double we = gemma ? (double)wf[e] + 1.0 : (double)wf[e];
-                                pm = __builtin_fmax(pm, __builtin_fabs((double)hf[e] * we));
-                            }
-                        }
-                    }
-                    st16(a.residual_out, base + j, hv[k]);
+                for (int e = 0; e < EPW; ++e) {
+                    const double hd = (double)hf[e];
+                    ss = __builtin_fma(hd, hd, ss);  // h^2 is exact in fp64
                 }
-            }
-        }
-
-        // ---- row reduction: wave DPP tree, then the row group's waves via LDS
-        ss = wave_sum_f64(ss);
-        if (fp8)
-            pm = wave_max_f64(pm);
-        if (wpr > 1) {
-            if (lane == 0) {
-                red[parity][wave][0] = ss;
-                red[parity][wave][1] = pm;
-            }
-            lds_barrier();
-            const int w0 = slot * wpr;
-            ss = red[parity][w0][0];
-            pm = red[parity][w0][1];
-            for (int w = 1; w < wpr; ++w) {
-                ss += red[parity][w0 + w][0];
-                pm = __builtin_fmax(pm, red[parity][w0 + w][1]);
-            }
-            parity ^= 1;
-        }
-
-        // ---- normalise, write the T output, FP8 epilogue
-        if (valid) {
-            const double rstd = 1.0 / __builtin_sqrt(ss / (double)a.H + (double)a.eps);
-            float scale = 0.0f, inv = 0.0f;
-            bool qfast = false;
-            if (fp8) {
-                // max |y| = RNE_T(max |h * w_eff| * rstd): rounding is monotone
-                const float amax = round_one<DT>(pm * rstd, exact_only);
-                scale = amax / 448.0f;
-                inv = 1.0f / scale;
-                qfast = !exact_only && scale >= 1.17549435e-38f && scale <= 3.0e38f;
-                if (lt == 0)
-                    a.fp8_scale[row] = scale;
-            }
-#pragma unroll
-            for (int k = 0; k < PPT; ++k) {
-                const int j = lt + k * tpr;
-                if (TAIL && j >= P)
-                    continue;
-                u32x4 yv;
-                bool risk = exact_only;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float hf[EPW], wf[EPW], yf[EPW];
-                    F::unpack(hv[k][i], hf);
+                if constexpr (FP8) {
+                    float wf[EPW];
                     F::unpack(wv[k][i], wf);
 #pragma unroll
                     for (int e = 0; e < EPW; ++e) {
                         const double we = gemma ? (double)wf[e] + 1.0 : (double)wf[e];
-                        yf[e] = (float)(((double)hf[e] * we) * rstd);
-                        risk |= F::tie_risk(yf[e]);
-                    }
-                    yv[i] = F::pack(yf);
-                }
-                if (risk) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float hf[EPW], wf[EPW], yf[EPW];
-                        F::unpack(hv[k][i], hf);
-                        F::unpack(wv[k][i], wf);
-#pragma unroll
-                        for (int e = 0; e < EPW; ++e) {
-                            const double we = gemma ? (double)wf[e] + 1.0 : (double)wf[e];
-                            yf[e] = F::exact(((double)hf[e] * we) * rstd);
-                        }
-                        yv[i] = F::pack(yf);
-                    }
-                }
-                if (a.out)
-                    st16(a.out, base + j, yv);
-                if constexpr (DT != DT_FP32) {
-                    if (fp8) {
-                        float y[8];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            float t[2];
-                            F::unpack(yv[i], t);
-                            y[2 * i] = t[0];
-                            y[2 * i + 1] = t[1];
-                        }
-                        u32x2 q = {0u, 0u};
-                        bool slow = !qfast;
-                        if (qfast) {
-                            float c[8];
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                c[e] = y[e] * inv;
-                                const uint32_t u = __float_as_uint(c[e]) & 0x7fffffffu;
-                                const uint32_t lo = u & 0xfffffu;
-                                // normal E4M3 range [2^-6, 464) and at least 4 fp32 ulps from
-                                // an E4M3 tie: y * (1/scale) then rounds like y / scale
-                                const bool ok = (u >= 0x3C800000u) & (u < 0x43E80000u) &
-                                                ((lo + 3u - 0x80000u) > 6u);
-                                slow |= !ok;
-                            }
-                            q.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
-                            q.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], (int)q.x, true);
-                            q.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
-                            q.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], (int)q.y, true);
-                        }
-                        if (slow) {
-                            uint32_t b[8];
-#pragma unroll
-                            for (int e = 0; e < 8; ++e)
-                                b[e] = scale == 0.0f ? ((__float_as_uint(y[e]) >> 24) & 0x80u)
-                                                     : e4m3_encode(y[e] / scale);
-                            q.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-                            q.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
-                        }
-                        ((u32x2 *)a.fp8_out)[base + j] = q;
+                        pm = __builtin_fmax(pm, __builtin_fabs((double)hf[e] * we));
                     }
                 }
             }
+            bstore(hv[k], rout, (uint32_t)(c.lt + k * c.tpr) * 16u);
+            // one pack at a time: keeps the fp64 temporaries of a single pack live
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
+
+    // ---- row reduction: wave DPP tree, then the row group's waves via LDS
+    ss = wave_sum_f64(ss);
+    if constexpr (FP8)
+        pm = wave_max_f64(pm);
+    if (c.wpr > 1) {
+        if (c.lane == 0) {
+            red[parity][c.wave][0] = ss;
+            red[parity][c.wave][1] = pm;
+        }
+        lds_barrier();
+        const int w0 = c.slot * c.wpr;
+        ss = red[parity][w0][0];
+        pm = red[parity][w0][1];
+        for (int w = 1; w < c.wpr; ++w) {
+            ss += red[parity][w0 + w][0];
+            if constexpr (FP8)
+                pm = __builtin_fmax(pm, red[parity][w0 + w][1]);
+        }
+        parity ^= 1;
+    }
+    if (!valid)
+        return;
+
+    // ---- normalise, write the T output, FP8 epilogue
+    const double rstd = 1.0 / __builtin_sqrt(ss / (double)a.H + (double)a.eps);
+    float scale = 0.0f, inv = 0.0f;
+    bool qfast = false;
+    if constexpr (FP8) {
+        // max |y| = RNE_T(max |h * w_eff| * rstd): rounding is monotone
+        const float amax = round_one<DT>(pm * rstd, exact_only);
+        scale = amax / 448.0f;
+        inv = 1.0f / scale;
+        qfast = !exact_only && scale >= 1.17549435e-38f && scale <= 3.0e38f;
+        if (c.lt == 0)
+            a.fp8_scale[row] = scale;
+    }
+    const __amdgpu_buffer_rsrc_t rout_t = row_rsrc(a.out, row, rb);
+    const __amdgpu_buffer_rsrc_t rout_q = row_rsrc(a.fp8_out, row, rb / 2);
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const uint32_t off = (uint32_t)(c.lt + k * c.tpr) * 16u;
+        u32x4 yv;
+        bool risk = exact_only;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float hf[EPW], wf[EPW], yf[EPW];
+            F::unpack(hv[k][i], hf);
+            F::unpack(wv[k][i], wf);
+#pragma unroll
+            for (int e = 0; e < EPW; ++e) {
+                const double we = gemma ? (double)wf[e] + 1.0 : (double)wf[e];
+                yf[e] = (float)(((double)hf[e] * we) * rstd);
+                risk |= F::tie_risk(yf[e]);
+            }
+            yv[i] = F::pack(yf);
+        }
+        if (risk) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float hf[EPW], wf[EPW], yf[EPW];
+                F::unpack(hv[k][i], hf);
+                F::unpack(wv[k][i], wf);
+#pragma unroll
+                for (int e = 0; e < EPW; ++e) {
+                    const double we = gemma ? (double)wf[e] + 1.0 : (double)wf[e];
+                    yf[e] = F::exact(((double)hf[e] * we) * rstd);
+                }
+                yv[i] = F::pack(yf);
+            }
+        }
+        if constexpr (OUT_T)
+            bstore(yv, rout_t, off);
+        if constexpr (FP8 && DT != DT_FP32) {
+            float y[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float t[2];
+                F::unpack(yv[i], t);
+                y[2 * i] = t[0];
+                y[2 * i + 1] = t[1];
+            }
+            u32x2 q = {0u, 0u};
+            bool slow = !qfast;
+            if (qfast) {
+                float cq[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    cq[e] = y[e] * inv;
+                    const uint32_t u = __float_as_uint(cq[e]) & 0x7fffffffu;
+                    const uint32_t lo = u & 0xfffffu;
+                    // normal E4M3 range [2^-6, 464) and at least 4 fp32 ulps from
+                    // an E4M3 tie: y * (1/scale) then rounds like y / scale
+                    const bool ok = (u >= 0x3C800000u) & (u < 0x43E80000u) &
+                                    ((lo + 3u - 0x80000u) > 6u);
+                    slow |= !ok;
+                }
+                q.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[0], cq[1], 0, false);
+                q.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[2], cq[3], (int)q.x, true);
+                q.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[4], cq[5], 0, false);
+                q.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[6], cq[7], (int)q.y, true);
+            }
+            if (slow) {
+                uint32_t qb[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    qb[e] = scale == 0.0f ? ((__float_as_uint(y[e]) >> 24) & 0x80u)
+                                          : e4m3_encode(y[e] / scale);
+                q.x = qb[0] | (qb[1] << 8) | (qb[2] << 16) | (qb[3] << 24);
+                q.y = qb[4] | (qb[5] << 8) | (qb[6] << 16) | (qb[7] << 24);
+            }
+            bstore8(q, rout_q, off / 2u);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int DT, int R, int PPT, int EPI>
+__global__ void __launch_bounds__(512) row_kernel(const RowArgs a)
+{
+    RowCtx c;
+    const int tid = threadIdx.x;
+    c.tpr = a.tpr;
+    c.wpr = c.tpr >> 6;
+    c.rpb = (int)blockDim.x / c.tpr;
+    // a wave never straddles two row groups (tpr is a multiple of 64), so the
+    // row-group index is wave-uniform: keep it in a scalar register
+    c.slot = __builtin_amdgcn_readfirstlane(tid / c.tpr);
+    c.lt = tid - c.slot * c.tpr;
+    c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    c.lane = tid & 63;
+    c.P = a.P;
+
+    __shared__ double red[2][kMaxWavesPerBlock][2];
+
+    u32x4 wv[PPT];
+    {
+        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)a.weight, (short)0, c.P * 16, kBufDword3);
+#pragma unroll
+        for (int k = 0; k < PPT; ++k)
+            wv[k] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (uint32_t)(c.lt + k * c.tpr) * 16u, 0, 0));
+    }
+
+    // One row group per block: every row is in flight at once (as far as the
+    // device holds the blocks), and the hardware dispatcher starts a new block
+    // as soon as one retires.
+    int parity = 0;
+    const long long g = blockIdx.x;
+    RowBuf<R, PPT> A;
+    load_rows<R, PPT>(a, c, g, A);
+    process_rows<DT, R, PPT, EPI>(a, c, g, A, wv, red, parity);
 }
 
 // --------------------------------------------------------------------------
@@ -431,7 +516,7 @@ ARRMS_DEV void flat_packs(const FlatArgs &a, const long long (&j)[kFlatPacksPerT
         if (ok[k]) {
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                xv[r][k] = ld16(a.in[r], j[k]);
+                xv[r][k] = ld16_nt(a.in[r], j[k]);
         }
 #pragma unroll
     for (int k = 0; k < kFlatPacksPerThread; ++k) {
@@ -473,45 +558,42 @@ __global__ void __launch_bounds__(kFlatThreads) flat_kernel(const FlatArgs a)
 
 // --------------------------------------------------------------------------
 // Launch helpers (instantiated per dtype by kern_*.hip).
-template <int DT, int R, int PPT>
+template <int DT, int R, int PPT, int EPI>
 static hipError_t row_go(const RowArgs &a, const RowShape &s, hipStream_t st)
 {
-    if constexpr (PPT * (R + 1) > 45) {
-        return hipErrorInvalidValue;  // register budget: never selected
-    } else {
-        dim3 grid((unsigned)s.grid), block((unsigned)(s.tpr * s.rpb));
-        if (s.tail)
-            hipLaunchKernelGGL((row_kernel<DT, R, PPT, true>), grid, block, 0, st, a);
-        else
-            hipLaunchKernelGGL((row_kernel<DT, R, PPT, false>), grid, block, 0, st, a);
-        return hipGetLastError();
-    }
+    const int block = s.tpr * s.rpb;
+    const long long groups = (a.M + s.rpb - 1) / s.rpb;
+    if (groups > 0x7fffffffLL)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((row_kernel<DT, R, PPT, EPI>), dim3((unsigned)groups), dim3((unsigned)block), 0, st,
+                       a);
+    return hipGetLastError();
 }
 
-template <int DT, int R>
+template <int DT, int R, int EPI>
 static hipError_t row_go_r(const RowArgs &a, const RowShape &s, hipStream_t st)
 {
     switch (s.ppt) {
-    case 1: return row_go<DT, R, 1>(a, s, st);
-    case 2: return row_go<DT, R, 2>(a, s, st);
-    case 4: return row_go<DT, R, 4>(a, s, st);
-    case 8: return row_go<DT, R, 8>(a, s, st);
+    case 1: return row_go<DT, R, 1, EPI>(a, s, st);
+    case 2: return row_go<DT, R, 2, EPI>(a, s, st);
+    case 4: return row_go<DT, R, 4, EPI>(a, s, st);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <int DT>
-static hipError_t row_launch(const RowArgs &a, int R, const RowShape &s, hipStream_t st)
+// One epilogue of one dtype: R = 1 .. 8.
+template <int DT, int EPI>
+static hipError_t row_launch_epi(const RowArgs &a, int R, const RowShape &s, hipStream_t st)
 {
     switch (R) {
-    case 1: return row_go_r<DT, 1>(a, s, st);
-    case 2: return row_go_r<DT, 2>(a, s, st);
-    case 3: return row_go_r<DT, 3>(a, s, st);
-    case 4: return row_go_r<DT, 4>(a, s, st);
-    case 5: return row_go_r<DT, 5>(a, s, st);
-    case 6: return row_go_r<DT, 6>(a, s, st);
-    case 7: return row_go_r<DT, 7>(a, s, st);
-    case 8: return row_go_r<DT, 8>(a, s, st);
+    case 1: return row_go_r<DT, 1, EPI>(a, s, st);
+    case 2: return row_go_r<DT, 2, EPI>(a, s, st);
+    case 3: return row_go_r<DT, 3, EPI>(a, s, st);
+    case 4: return row_go_r<DT, 4, EPI>(a, s, st);
+    case 5: return row_go_r<DT, 5, EPI>(a, s, st);
+    case 6: return row_go_r<DT, 6, EPI>(a, s, st);
+    case 7: return row_go_r<DT, 7, EPI>(a, s, st);
+    case 8: return row_go_r<DT, 8, EPI>(a, s, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -29,7 +29,6 @@ struct RowArgs {
     int tpr;              // threads per row group (multiple of 64)
     float eps;
     int gemma;
-    int fp8;
     int exact_only;
 };
 
@@ -41,22 +40,28 @@ struct FlatArgs {
 };
 
 // Row kernel shape: PPT packs per thread per row, tpr threads per row,
-// rpb rows per block; tail = tpr * PPT > packs per row.
+// rpb rows per block (one block per group of rpb rows); tail = tpr * PPT >
+// packs per row.
 struct RowShape {
     int ppt;
     int tpr;
     int rpb;
     bool tail;
-    int grid;
 };
 
 constexpr int kFlatThreads = 256;
 constexpr int kFlatPacksPerThread = 2;
 constexpr int kFlatTile = kFlatThreads * kFlatPacksPerThread;
 
-hipError_t launch_row_bf16(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
-hipError_t launch_row_fp16(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
-hipError_t launch_row_fp32(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
+// Row kernels, one entry per dtype and epilogue (kern_<dtype>_<epilogue>.hip):
+// _t writes the T output, _fp8 the FP8 output only, _fp8t FP8 plus the T mirror.
+hipError_t launch_row_bf16_t(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
+hipError_t launch_row_bf16_fp8(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
+hipError_t launch_row_bf16_fp8t(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
+hipError_t launch_row_fp16_t(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
+hipError_t launch_row_fp16_fp8(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
+hipError_t launch_row_fp16_fp8t(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
+hipError_t launch_row_fp32_t(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
 hipError_t launch_flat_bf16(const FlatArgs &a, int R, hipStream_t st);
 hipError_t launch_flat_fp16(const FlatArgs &a, int R, hipStream_t st);
 hipError_t launch_flat_fp32(const FlatArgs &a, int R, hipStream_t st);

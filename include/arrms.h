@@ -112,6 +112,22 @@ ARRMS_API int arrms_fused(const void *const *rank_in, int R, const void *residua
                 float eps, int flags, hipStream_t stream);
 
 /*
+ * arrms_fused_config -- arrms_fused with an explicit launch shape for the row
+ * kernel, for benchmarking and tuning (the automatic choice is the shape
+ * arrms_fused takes). ppt: 16-byte packs per thread and row (1, 2 or 4); tpr:
+ * threads per row (a multiple of 64, at most 512, tpr * ppt covering the row);
+ * rows_per_block: rows handled side by side by one block (tpr *
+ * rows_per_block <= 512). 0 in any of them keeps the automatic value; a
+ * negative value gives ARRMS_ERR_INVALID and a shape that cannot cover a row
+ * ARRMS_ERR_UNSUPPORTED. All other arguments, the results and the error
+ * behaviour are arrms_fused's.
+ */
+ARRMS_API int arrms_fused_config(const void *const *rank_in, int R, const void *residual,
+                                 const void *weight, void *out, void *residual_out, void *fp8_out,
+                                 float *fp8_scale, int M, int H, float eps, int flags, int ppt,
+                                 int tpr, int rows_per_block, hipStream_t stream);
+
+/*
  * arrms_reserve_staging -- allocate the staging buffer of the two-stage path
  * on the current device, at least `bytes` (0: ARRMS_DEFAULT_STAGING_BYTES), the
  * per-rank staging region of PR #6699 Changes. A larger existing buffer is
