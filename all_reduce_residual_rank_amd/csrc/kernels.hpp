@@ -213,11 +213,6 @@ ARRMS_DEV void st16_nt(void *p, long long i, u32x4 v) { __builtin_nontemporal_st
 // T mirror.
 enum Epilogue { EPI_T = 0, EPI_FP8 = 1, EPI_FP8_T = 2 };
 
-template <int R, int PPT> struct RowBuf {
-    u32x4 x[R][PPT];
-    u32x4 res[PPT];
-};
-
 struct RowCtx {
     int lt;      // thread index within the row group
     int tpr;     // threads per row group
@@ -260,36 +255,32 @@ ARRMS_DEV void bstore8(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
     __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kBufAuxNT);
 }
 
-template <int R, int PPT>
-ARRMS_DEV void load_rows(const RowArgs &a, const RowCtx &c, long long g, RowBuf<R, PPT> &b)
+// Phase 1 streams through the thread's packs with a prefetch distance of
+// kPrefetch packs: the loads of pack k + kPrefetch (all R inputs and the
+// residual) are issued before pack k is reduced. A handful of 16-byte loads
+// in flight per wave keeps HBM busy across the resident blocks; issuing all of
+// a row's loads at once measured slower on MI355X and costs registers.
+constexpr int kPrefetch = 1;
+
+template <int R>
+ARRMS_DEV void load_pack(const __amdgpu_buffer_rsrc_t (&rs)[R + 1], uint32_t off, u32x4 (&x)[R + 1])
 {
-    const long long row = g * c.rpb + c.slot;
-    if (row >= a.M)
-        return;
-    const int rb = c.P * 16;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.in[r], row, rb);
-#pragma unroll
-        for (int k = 0; k < PPT; ++k)
-            b.x[r][k] = bload(rs, (uint32_t)(c.lt + k * c.tpr) * 16u);
-    }
-    const __amdgpu_buffer_rsrc_t rs = row_rsrc(a.residual, row, rb);
-#pragma unroll
-    for (int k = 0; k < PPT; ++k)
-        b.res[k] = bload(rs, (uint32_t)(c.lt + k * c.tpr) * 16u);
+    for (int r = 0; r <= R; ++r)
+        x[r] = bload(rs[r], off);
 }
 
 template <int DT, int R, int PPT, int EPI>
-ARRMS_DEV void process_rows(const RowArgs &a, const RowCtx &c, long long g, const RowBuf<R, PPT> &b,
-                            const u32x4 (&wv)[PPT], double (&red)[2][kMaxWavesPerBlock][2],
-                            int &parity)
+ARRMS_DEV void process_rows(const RowArgs &a, const RowCtx &c, long long g, const u32x4 (&wv)[PPT],
+                            double (&red)[2][kMaxWavesPerBlock][2], int &parity)
 {
     using F = Fmt<DT>;
     constexpr int EPW = F::EPW;
     constexpr bool FP8 = (EPI != EPI_T);
     constexpr bool OUT_T = (EPI != EPI_FP8);
-    const bool gemma = a.gemma != 0;
+    // w_eff = w + gadd: 1 under gemma_norm, else -0.0, which adds nothing to
+    // any value (signed zeros included), so one fp64 add serves both modes
+    const double gadd = a.gemma ? 1.0 : -0.0;
     const bool exact_only = a.exact_only != 0;
     const long long row = g * c.rpb + c.slot;
     const bool valid = row < a.M;
@@ -297,55 +288,69 @@ ARRMS_DEV void process_rows(const RowArgs &a, const RowCtx &c, long long g, cons
 
     // ---- rank sum, residual add, sum of squares (and max |h * w_eff|)
     u32x4 hv[PPT];
-    double ss = 0.0;
+    double ssw[4] = {0.0, 0.0, 0.0, 0.0};  // one partial sum of squares per word
     double pm = 0.0;
     if (valid) {
+        __amdgpu_buffer_rsrc_t rs[R + 1];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            rs[r] = row_rsrc(a.in[r], row, rb);
+        rs[R] = row_rsrc(a.residual, row, rb);
         const __amdgpu_buffer_rsrc_t rout = row_rsrc(a.residual_out, row, rb);
+        constexpr int D = kPrefetch < PPT ? kPrefetch : PPT;
+        u32x4 ring[D + 1][R + 1];
+#pragma unroll
+        for (int k = 0; k < D; ++k)
+            load_pack<R>(rs, (uint32_t)(c.lt + k * c.tpr) * 16u, ring[k % (D + 1)]);
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
+            if (k + D < PPT)
+                load_pack<R>(rs, (uint32_t)(c.lt + (k + D) * c.tpr) * 16u, ring[(k + D) % (D + 1)]);
+            __builtin_amdgcn_sched_barrier(0);
+            const u32x4 (&x)[R + 1] = ring[k % (D + 1)];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float acc[EPW];
-                F::unpack(b.x[0][k][i], acc);
+                F::unpack(x[0][i], acc);
 #pragma unroll
                 for (int r = 1; r < R; ++r) {
                     float t[EPW];
-                    F::unpack(b.x[r][k][i], t);
+                    F::unpack(x[r][i], t);
 #pragma unroll
                     for (int e = 0; e < EPW; ++e)
                         acc[e] = acc[e] + t[e];
                 }
-                float av[EPW], rs[EPW], hf[EPW];
+                float av[EPW], rsd[EPW], hf[EPW];
                 F::unpack(F::pack(acc), av);  // a = RNE_T(sum)
-                F::unpack(b.res[k][i], rs);
+                F::unpack(x[R][i], rsd);
 #pragma unroll
                 for (int e = 0; e < EPW; ++e)
-                    acc[e] = av[e] + rs[e];
+                    acc[e] = av[e] + rsd[e];
                 const uint32_t hw = F::pack(acc);  // h = RNE_T(a + res)
                 hv[k][i] = hw;
                 F::unpack(hw, hf);
 #pragma unroll
                 for (int e = 0; e < EPW; ++e) {
                     const double hd = (double)hf[e];
-                    ss = __builtin_fma(hd, hd, ss);  // h^2 is exact in fp64
+                    ssw[i] = __builtin_fma(hd, hd, ssw[i]);  // h^2 is exact in fp64
                 }
                 if constexpr (FP8) {
                     float wf[EPW];
                     F::unpack(wv[k][i], wf);
 #pragma unroll
                     for (int e = 0; e < EPW; ++e) {
-                        const double we = gemma ? (double)wf[e] + 1.0 : (double)wf[e];
+                        const double we = (double)wf[e] + gadd;
                         pm = __builtin_fmax(pm, __builtin_fabs((double)hf[e] * we));
                     }
                 }
             }
             bstore(hv[k], rout, (uint32_t)(c.lt + k * c.tpr) * 16u);
-            // one pack at a time: keeps the fp64 temporaries of a single pack live
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 
     // ---- row reduction: wave DPP tree, then the row group's waves via LDS
+    double ss = (ssw[0] + ssw[1]) + (ssw[2] + ssw[3]);
     ss = wave_sum_f64(ss);
     if constexpr (FP8)
         pm = wave_max_f64(pm);
@@ -395,7 +400,7 @@ ARRMS_DEV void process_rows(const RowArgs &a, const RowCtx &c, long long g, cons
             F::unpack(wv[k][i], wf);
 #pragma unroll
             for (int e = 0; e < EPW; ++e) {
-                const double we = gemma ? (double)wf[e] + 1.0 : (double)wf[e];
+                const double we = (double)wf[e] + gadd;
                 yf[e] = (float)(((double)hf[e] * we) * rstd);
                 risk |= F::tie_risk(yf[e]);
             }
@@ -409,7 +414,7 @@ ARRMS_DEV void process_rows(const RowArgs &a, const RowCtx &c, long long g, cons
                 F::unpack(wv[k][i], wf);
 #pragma unroll
                 for (int e = 0; e < EPW; ++e) {
-                    const double we = gemma ? (double)wf[e] + 1.0 : (double)wf[e];
+                    const double we = (double)wf[e] + gadd;
                     yf[e] = F::exact(((double)hf[e] * we) * rstd);
                 }
                 yv[i] = F::pack(yf);
@@ -457,7 +462,6 @@ ARRMS_DEV void process_rows(const RowArgs &a, const RowCtx &c, long long g, cons
             }
             bstore8(q, rout_q, off / 2u);
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -493,10 +497,7 @@ __global__ void __launch_bounds__(512) row_kernel(const RowArgs a)
     // device holds the blocks), and the hardware dispatcher starts a new block
     // as soon as one retires.
     int parity = 0;
-    const long long g = blockIdx.x;
-    RowBuf<R, PPT> A;
-    load_rows<R, PPT>(a, c, g, A);
-    process_rows<DT, R, PPT, EPI>(a, c, g, A, wv, red, parity);
+    process_rows<DT, R, PPT, EPI>(a, c, (long long)blockIdx.x, wv, red, parity);
 }
 
 // --------------------------------------------------------------------------
