@@ -1,0 +1,120 @@
+"""Summaries of rocprofv3 runs of bench.py: per-kernel durations and HBM traffic.
+
+Usage (paths are the rocprofv3 output directories of one command each):
+  python -m all_reduce_residual_rank_amd.prof --trace DIR --fetch DIR --write DIR \\
+      --workload NAME --path one --command "..." --out profiles/NAME.md
+
+FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
+counters read for a plain device-to-device copy of known size (bench.py
+--calibrate-copy: 256 MiB read and 256 MiB written), so that the reported
+traffic is in bytes of HBM reads and writes.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import statistics
+
+COPY_BYTES = 256 << 20
+
+
+def _csv(d, suffix):
+    f = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+    if not f:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return list(csv.DictReader(open(f[0])))
+
+
+def kernel_stats(trace_dir):
+    """Average/min/max/count of each kernel's duration (ns) from the kernel trace."""
+    rows = _csv(trace_dir, "kernel_trace.csv")
+    by = {}
+    for r in rows:
+        d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        by.setdefault(r["Kernel_Name"], []).append(d)
+    return {k: {"count": len(v), "avg_ns": statistics.mean(v), "median_ns": statistics.median(v),
+                "min_ns": min(v), "max_ns": max(v)} for k, v in by.items()}
+
+
+def counter(dir_, name):
+    rows = _csv(dir_, "counter_collection.csv")
+    by = {}
+    for r in rows:
+        if r["Counter_Name"] == name:
+            by.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return by
+
+
+def copy_kernel(names):
+    for n in names:
+        if "copyBuffer" in n or "copy" in n.lower():
+            return n
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--path", required=True)
+    ap.add_argument("--command", required=True)
+    ap.add_argument("--digest", required=True)
+    ap.add_argument("--algo-bytes", type=int, required=True)
+    ap.add_argument("--bench-us", type=float, required=True, help="bench.py us/call of the same command")
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--traffic-json", required=True)
+    a = ap.parse_args()
+
+    ks = kernel_stats(a.trace)
+    fetch = counter(a.fetch, "FETCH_SIZE")
+    write = counter(a.write, "WRITE_SIZE")
+    ck = copy_kernel(fetch)
+    # the copy may be split into several dispatches: scale by the total over one copy
+    f_copy = sum(fetch[ck]) / 4.0 if ck else None
+    w_copy = sum(write.get(ck, [])) / 4.0 if ck else None
+    f_scale = COPY_BYTES / (f_copy * 1024.0) if f_copy else None
+    w_scale = COPY_BYTES / (w_copy * 1024.0) if w_copy else None
+    ours = [k for k in ks if "arrms::" in k]
+    lines = [f"# rocprofv3 summary: {a.workload}, path {a.path}", "",
+             "Command (run from the repository root, one run per block below):", "",
+             "```", f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- {a.command}",
+             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- {a.command}",
+             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- {a.command}", "```", "",
+             f"Kernel sources digest: `{a.digest}`. bench.py us/call of the same command: {a.bench_us:.3f}.",
+             "", "| kernel | dispatches | avg us | median us | min us | max us |", "|---|---|---|---|---|---|"]
+    for k in sorted(ks, key=lambda k: -ks[k]["avg_ns"] * ks[k]["count"]):
+        v = ks[k]
+        lines.append(f"| `{k[:90]}` | {v['count']} | {v['avg_ns']/1e3:.3f} | {v['median_ns']/1e3:.3f} | "
+                     f"{v['min_ns']/1e3:.3f} | {v['max_ns']/1e3:.3f} |")
+    lines += ["", "HBM traffic per dispatch (counter KiB scaled by the 256 MiB copy's reading):", ""]
+    if ck:
+        lines.append(f"- copy kernel `{ck}`: FETCH_SIZE {f_copy:.0f} KiB, WRITE_SIZE {w_copy:.0f} KiB per "
+                     f"256 MiB copy -> scale factors {f_scale:.4f} (reads), {w_scale:.4f} (writes)")
+    traffic = {}
+    for k in ours:
+        if k not in fetch:
+            continue
+        fr = statistics.mean(fetch[k]) * 1024.0 * (f_scale or 1.0)
+        wr = statistics.mean(write.get(k, [0.0])) * 1024.0 * (w_scale or 1.0)
+        lines.append(f"- `{k[:90]}`: reads {fr/1e6:.2f} MB, writes {wr/1e6:.2f} MB, total {(fr+wr)/1e6:.2f} MB "
+                     f"(algorithmic {a.algo_bytes/1e6:.2f} MB per call)")
+        traffic[k] = fr + wr
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    db = {}
+    if os.path.exists(a.traffic_json):
+        db = json.load(open(a.traffic_json))
+    db[f"{a.workload}/{a.path}"] = {"sources_digest": a.digest,
+                                     "hbm_bytes_per_launch": round(sum(traffic.values())),
+                                     "per_kernel_bytes": {k[:90]: round(v) for k, v in traffic.items()},
+                                     "summary": os.path.basename(a.out)}
+    json.dump(db, open(a.traffic_json, "w"), indent=1)
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()

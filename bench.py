@@ -43,7 +43,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="bound on the CPU-baseline work")
-    p.add_argument("--quiet", action="store_true")
+    p.add_argument("--no-other-path", action="store_true", help="time only the chosen path")
+    p.add_argument("--no-hot", action="store_true", help="skip the cache-resident context number")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run a plain 256 MiB device-to-device copy (4 times) so that a "
+                        "profiler's FETCH_SIZE/WRITE_SIZE can be scaled by a kernel of known size")
     return p.parse_args()
 
 
@@ -195,6 +199,13 @@ def main():
 
     wl = wlmod.BY_NAME[args.workload]
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     e = wl.esize
     set_bytes = (wl.R + 3) * wl.M * wl.H * e
     nsets = max(2, -(-ROTATE_BYTES // set_bytes))
@@ -219,10 +230,10 @@ def main():
     for p in ("one", "two"):
         if p == chosen:
             other[p] = round(us, 3)
-        else:
+        elif not args.no_other_path:
             ms2 = time_path(torch, arrms, wl, sets, wl.flags | path_flags[p], args.steps, args.warmup)
             other[p] = round(ms2 * 1000.0 / args.steps, 3)
-    hot = time_hot(torch, arrms, wl, sets, wl.flags | path_flags[chosen])
+    hot = None if args.no_hot else time_hot(torch, arrms, wl, sets, wl.flags | path_flags[chosen])
     digest = sources_digest()
     traffic = load_traffic(wl.name, chosen, digest)
 
@@ -236,7 +247,7 @@ def main():
                    "compute": "fp32 rank sums, fp64 row statistics"},
         "us_per_call": round(us, 3), "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
         "metric_bytes": metric_bytes,
-        "path_us": other, "hot_us_cache_resident": round(hot, 3),
+        "path_us": other, "hot_us_cache_resident": None if hot is None else round(hot, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": algo_bytes,
