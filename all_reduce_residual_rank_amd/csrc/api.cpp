@@ -150,8 +150,10 @@ int choose_path(int M, int H, int R, int flags)
 // multiple of 64 up to 512. Prefer an exact cover (no idle lanes), then the
 // least padding, then more packs per thread (fewer, busier threads: measured
 // faster on MI355X) as long as a thread's R+1 input packs stay within 20
-// (80 registers), which keeps several blocks resident per compute unit.
-arrms::RowShape choose_shape(int P, int R, long long M)
+// (80 registers), which keeps several blocks resident per compute unit. The
+// FP8 epilogue has more per-element work after the row reduction; spreading
+// it over more threads (at most 2 packs each) measured faster.
+arrms::RowShape choose_shape(int P, int R, long long M, bool fp8)
 {
     (void)M;
     arrms::RowShape best = {0, 0, 0, false};
@@ -160,6 +162,8 @@ arrms::RowShape choose_shape(int P, int R, long long M)
     for (int c = 0; c < 3; ++c) {
         const int ppt = ppts[c];
         if (ppt > 1 && ppt * (R + 1) > 20)
+            continue;
+        if (fp8 && ppt > 2)
             continue;
         int tpr = (P + ppt - 1) / ppt;
         tpr = (tpr + 63) / 64 * 64;
@@ -390,7 +394,7 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
         for (int r = 0; r < R; ++r)
             a.in[r] = rank_in[r];
         a.M = M;
-        arrms::RowShape s = choose_shape(P, R, M);
+        arrms::RowShape s = choose_shape(P, R, M, fp8);
         if (s.ppt == 0 || !apply_shape(req, P, R, M, s))
             return ARRMS_ERR_UNSUPPORTED;
         a.tpr = s.tpr;
@@ -449,7 +453,7 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
         b.M = n;
         // the row pass takes the one-stage shape of these rows, so both paths
         // reduce the row statistics in the same order and give the same bits
-        arrms::RowShape s = choose_shape(P, R, n);
+        arrms::RowShape s = choose_shape(P, R, n, fp8);
         if (s.ppt == 0 || !apply_shape(req, P, R, n, s))
             return ARRMS_ERR_UNSUPPORTED;
         b.tpr = s.tpr;

@@ -140,8 +140,8 @@ ARRMS_DEV uint32_t e4m3_encode(float x)
 
 // --------------------------------------------------------------------------
 // Wave (64-lane) reductions of fp64 values: DPP within rows of 16 lanes,
-// ds_bpermute across rows. Every lane ends with the same bits (each step adds
-// the same two operands on both partner lanes).
+// permlane swaps across rows. Every lane ends with the same bits (each step
+// adds the same two operands on both partner lanes).
 template <int CTRL> ARRMS_DEV double dpp_f64(double v)
 {
     u32x2 w = __builtin_bit_cast(u32x2, v);
@@ -150,14 +150,48 @@ template <int CTRL> ARRMS_DEV double dpp_f64(double v)
     return __builtin_bit_cast(double, w);
 }
 
-ARRMS_DEV double xor_lanes_f64(double v, int mask)
+// Partner value across 16-lane rows: v_permlane16_swap / v_permlane32_swap
+// (gfx950) exchange a register between lanes i and i^16 / i^32 without LDS.
+// Each builtin returns the two swapped registers; with both operands equal to
+// v, the pair holds v of lane i and v of lane i^m in an order that depends on
+// the lane, so a sum of the pair is the same on both partner lanes.
+template <bool ROW32> ARRMS_DEV u32x2 swap_pair(uint32_t x)
 {
-    int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    int addr = (lane ^ mask) << 2;
-    u32x2 w = __builtin_bit_cast(u32x2, v);
-    w.x = __builtin_amdgcn_ds_bpermute(addr, w.x);
-    w.y = __builtin_amdgcn_ds_bpermute(addr, w.y);
-    return __builtin_bit_cast(double, w);
+    u32x2 r;
+    if constexpr (ROW32) {
+        auto t = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        r.x = t[0];
+        r.y = t[1];
+    } else {
+        auto t = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        r.x = t[0];
+        r.y = t[1];
+    }
+    return r;
+}
+
+// (value of this lane, value of the partner lane), in a lane-dependent order
+template <bool ROW32> ARRMS_DEV void pair_f64(double v, double &a, double &b)
+{
+    const u32x2 w = __builtin_bit_cast(u32x2, v);
+    const u32x2 lo = swap_pair<ROW32>(w.x);
+    const u32x2 hi = swap_pair<ROW32>(w.y);
+    a = __builtin_bit_cast(double, u32x2{lo.x, hi.x});
+    b = __builtin_bit_cast(double, u32x2{lo.y, hi.y});
+}
+
+template <bool ROW32> ARRMS_DEV double sum_across(double v)
+{
+    double a, b;
+    pair_f64<ROW32>(v, a, b);
+    return a + b;
+}
+
+template <bool ROW32> ARRMS_DEV double max_across(double v)
+{
+    double a, b;
+    pair_f64<ROW32>(v, a, b);
+    return __builtin_fmax(a, b);
 }
 
 ARRMS_DEV double wave_sum_f64(double v)
@@ -166,8 +200,8 @@ ARRMS_DEV double wave_sum_f64(double v)
     v += dpp_f64<0x4E>(v);   // quad_perm [2,3,0,1]
     v += dpp_f64<0x141>(v);  // row_half_mirror
     v += dpp_f64<0x140>(v);  // row_mirror
-    v += xor_lanes_f64(v, 16);
-    v += xor_lanes_f64(v, 32);
+    v = sum_across<false>(v);  // rows 0+1, 2+3
+    v = sum_across<true>(v);   // halves
     return v;
 }
 
@@ -177,8 +211,8 @@ ARRMS_DEV double wave_max_f64(double v)
     v = __builtin_fmax(v, dpp_f64<0x4E>(v));
     v = __builtin_fmax(v, dpp_f64<0x141>(v));
     v = __builtin_fmax(v, dpp_f64<0x140>(v));
-    v = __builtin_fmax(v, xor_lanes_f64(v, 16));
-    v = __builtin_fmax(v, xor_lanes_f64(v, 32));
+    v = max_across<false>(v);
+    v = max_across<true>(v);
     return v;
 }
 
@@ -281,6 +315,8 @@ ARRMS_DEV void process_rows(const RowArgs &a, const RowCtx &c, long long g, cons
     // w_eff = w + gadd: 1 under gemma_norm, else -0.0, which adds nothing to
     // any value (signed zeros included), so one fp64 add serves both modes
     const double gadd = a.gemma ? 1.0 : -0.0;
+    // plain weights with 16-bit data: the product h * w needs no fp64
+    const bool plain_product = DT != DT_FP32 && !a.gemma;
     const bool exact_only = a.exact_only != 0;
     const long long row = g * c.rpb + c.slot;
     const bool valid = row < a.M;
@@ -393,18 +429,35 @@ ARRMS_DEV void process_rows(const RowArgs &a, const RowCtx &c, long long g, cons
         const uint32_t off = (uint32_t)(c.lt + k * c.tpr) * 16u;
         u32x4 yv;
         bool risk = exact_only;
+        if (plain_product) {
+            // h * w is exact in fp32 (at most 8 + 8 or 11 + 11 significant bits),
+            // so fl64(h * w) = (double)(h * w): one conversion instead of two
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float hf[EPW], wf[EPW], yf[EPW];
-            F::unpack(hv[k][i], hf);
-            F::unpack(wv[k][i], wf);
+            for (int i = 0; i < 4; ++i) {
+                float hf[EPW], wf[EPW], yf[EPW];
+                F::unpack(hv[k][i], hf);
+                F::unpack(wv[k][i], wf);
 #pragma unroll
-            for (int e = 0; e < EPW; ++e) {
-                const double we = (double)wf[e] + gadd;
-                yf[e] = (float)(((double)hf[e] * we) * rstd);
-                risk |= F::tie_risk(yf[e]);
+                for (int e = 0; e < EPW; ++e) {
+                    yf[e] = (float)((double)(hf[e] * wf[e]) * rstd);
+                    risk |= F::tie_risk(yf[e]);
+                }
+                yv[i] = F::pack(yf);
             }
-            yv[i] = F::pack(yf);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float hf[EPW], wf[EPW], yf[EPW];
+                F::unpack(hv[k][i], hf);
+                F::unpack(wv[k][i], wf);
+#pragma unroll
+                for (int e = 0; e < EPW; ++e) {
+                    const double we = (double)wf[e] + gadd;
+                    yf[e] = (float)(((double)hf[e] * we) * rstd);
+                    risk |= F::tie_risk(yf[e]);
+                }
+                yv[i] = F::pack(yf);
+            }
         }
         if (risk) {
 #pragma unroll
