@@ -43,12 +43,19 @@ MAX_HIDDEN = 16384
 DEFAULT_STAGING_BYTES = 16 << 20
 PATH_NONE, PATH_ONE_STAGE, PATH_TWO_STAGE = 0, 1, 2
 
-EXPORTS = ("arrms_fused", "arrms_fused_config", "arrms_reserve_staging", "arrms_release_staging",
-           "arrms_staging_bytes", "arrms_query_path", "arrms_status_string")
+EXPORTS = ("arrms_fused", "arrms_fused_strided", "arrms_allreduce_sum", "arrms_fused_config",
+           "arrms_reserve_staging", "arrms_release_staging", "arrms_staging_bytes", "arrms_query_path",
+           "arrms_status_string")
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_ll = ctypes.c_longlong
 _lib.arrms_fused.argtypes = [ctypes.POINTER(_vp), _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _vp]
 _lib.arrms_fused.restype = _i
+_lib.arrms_fused_strided.argtypes = [ctypes.POINTER(_vp), _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
+                                     _ll, _ll, _ll, _ll, _ll, _f, _i, _vp]
+_lib.arrms_fused_strided.restype = _i
+_lib.arrms_allreduce_sum.argtypes = [ctypes.POINTER(_vp), _i, _vp, _ll, _i, _vp]
+_lib.arrms_allreduce_sum.restype = _i
 _lib.arrms_fused_config.argtypes = [ctypes.POINTER(_vp), _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i,
                                     _i, _i, _i, _vp]
 _lib.arrms_fused_config.restype = _i
@@ -139,6 +146,66 @@ def arrms_fused(rank_in, residual, weight, out, residual_out, fp8_out=None, fp8_
                          fp8_scale, M, H, eps, flags, st)
     if rc != OK:
         raise ArrmsError(rc, "arrms_fused")
+
+
+def arrms_fused_strided_raw(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale,
+                            M, H, ld_in, ld_residual, ld_out, ld_residual_out, ld_fp8, eps, flags,
+                            stream) -> int:
+    """arrms_fused_strided with addresses as ints; returns the status unchanged."""
+    ptrs = (_vp * max(len(rank_in), 1))(*[_addr(p) for p in rank_in])
+    return _lib.arrms_fused_strided(ptrs, int(R), _addr(residual), _addr(weight), _addr(out),
+                                    _addr(residual_out), _addr(fp8_out), _addr(fp8_scale), int(M),
+                                    int(H), int(ld_in), int(ld_residual), int(ld_out),
+                                    int(ld_residual_out), int(ld_fp8), float(eps), int(flags), stream)
+
+
+def _row_stride(t, default: int) -> int:
+    if t is None or isinstance(t, int):
+        return default
+    if t.dim() < 2 or t.stride(-1) != 1:
+        raise ValueError("strided rows need a unit stride along the last dimension")
+    return int(t.stride(-2))
+
+
+def arrms_fused_strided(rank_in, residual, weight, out, residual_out, fp8_out=None, fp8_scale=None, *,
+                        eps: float, flags: int, M: int | None = None, H: int | None = None,
+                        ld_in: int | None = None, ld_residual: int | None = None,
+                        ld_out: int | None = None, ld_residual_out: int | None = None,
+                        ld_fp8: int | None = None, stream=None) -> None:
+    """arrms_fused over row-strided matrices (for instance column slices of
+    wider tensors). Strides default to each tensor's own row stride."""
+    if M is None or H is None:
+        M, H = residual.shape[-2], residual.shape[-1]
+    if ld_in is None:
+        strides = {_row_stride(t, H) for t in rank_in}
+        if len(strides) != 1:
+            raise ValueError("all rank inputs must share one row stride")
+        ld_in = strides.pop()
+    ld_residual = _row_stride(residual, H) if ld_residual is None else ld_residual
+    ld_out = _row_stride(out, H) if ld_out is None else ld_out
+    ld_residual_out = _row_stride(residual_out, H) if ld_residual_out is None else ld_residual_out
+    ld_fp8 = _row_stride(fp8_out, H) if ld_fp8 is None else ld_fp8
+    rc = arrms_fused_strided_raw(rank_in, len(rank_in), residual, weight, out, residual_out, fp8_out,
+                                 fp8_scale, M, H, ld_in, ld_residual, ld_out, ld_residual_out, ld_fp8,
+                                 eps, flags, _stream_handle(stream))
+    if rc != OK:
+        raise ArrmsError(rc, "arrms_fused_strided")
+
+
+def arrms_allreduce_sum_raw(rank_in, R, out, n, flags, stream) -> int:
+    """arrms_allreduce_sum with addresses as ints; returns the status unchanged."""
+    ptrs = (_vp * max(len(rank_in), 1))(*[_addr(p) for p in rank_in])
+    return _lib.arrms_allreduce_sum(ptrs, int(R), _addr(out), int(n), int(flags), stream)
+
+
+def arrms_allreduce_sum(rank_in, out, *, flags: int, n: int | None = None, stream=None) -> None:
+    """Enqueue the rank-ordered sum of the R rank tensors into ``out``
+    (contiguous tensors of n elements; n defaults to out.numel())."""
+    if n is None:
+        n = out.numel()
+    rc = arrms_allreduce_sum_raw(rank_in, len(rank_in), out, n, flags, _stream_handle(stream))
+    if rc != OK:
+        raise ArrmsError(rc, "arrms_allreduce_sum")
 
 
 def arrms_reserve_staging(nbytes: int = 0) -> None:

@@ -37,9 +37,20 @@ struct Span {
 bool overlaps(const Span &a, const Span &b) { return a.lo < b.hi && b.lo < a.hi; }
 
 // Checks that need no device: sizes, flags, pointers, alignment, overlap.
+// Row strides of the fused call, in elements of each tensor (fp8: bytes).
+struct Strides {
+    long long in, res, out, rout, q;
+};
+
+// Bytes spanned by a strided [M][H] matrix: (M - 1) rows of ld plus one row.
+uintptr_t span_bytes(int M, int H, long long ld, int e)
+{
+    return (uintptr_t)(M - 1) * (uintptr_t)ld * (uintptr_t)e + (uintptr_t)H * (uintptr_t)e;
+}
+
 int validate(const void *const *rank_in, int R, const void *residual, const void *weight,
              const void *out, const void *residual_out, const void *fp8_out,
-             const float *fp8_scale, int M, int H, float eps, int flags)
+             const float *fp8_scale, int M, int H, float eps, int flags, const Strides &ld)
 {
     if (flags & ~kKnownFlags)
         return ARRMS_ERR_INVALID;
@@ -76,25 +87,43 @@ int validate(const void *const *rank_in, int R, const void *residual, const void
         return ARRMS_ERR_UNSUPPORTED;
     if (fp8 && (!aligned16(fp8_out) || ((uintptr_t)fp8_scale & 3u)))
         return ARRMS_ERR_UNSUPPORTED;
+    // strides: at least a row, rows 16-byte aligned
+    const int e = esize(dt);
+    const long long lds[4] = {ld.in, ld.res, ld.out, ld.rout};
+    for (int i = 0; i < 4; ++i) {
+        if (lds[i] < H)
+            return ARRMS_ERR_INVALID;
+        if ((lds[i] * e) % 16 != 0)
+            return ARRMS_ERR_UNSUPPORTED;
+    }
+    if (fp8) {
+        // FP8 codes go out 8 bytes per pack: rows must start 8-byte aligned
+        if (ld.q < H)
+            return ARRMS_ERR_INVALID;
+        if (ld.q % 8 != 0)
+            return ARRMS_ERR_UNSUPPORTED;
+    }
+    const bool inplace = residual_out == residual;
+    if (inplace && ld.rout != ld.res)
+        return ARRMS_ERR_INVALID;
 
-    // overlap: outputs against inputs and against each other
-    const uintptr_t mat = (uintptr_t)M * (uintptr_t)H * (uintptr_t)esize(dt);
+    // overlap: outputs against inputs and against each other (a strided matrix
+    // counts as the whole byte range from its first to its last element)
     if (M == 0)
         return ARRMS_OK;
     Span ins[ARRMS_MAX_RANKS + 2];
     int nin = 0;
     for (int r = 0; r < R; ++r)
-        ins[nin++] = {(uintptr_t)rank_in[r], (uintptr_t)rank_in[r] + mat};
-    const Span res_span = {(uintptr_t)residual, (uintptr_t)residual + mat};
-    ins[nin++] = {(uintptr_t)weight, (uintptr_t)weight + (uintptr_t)H * esize(dt)};
+        ins[nin++] = {(uintptr_t)rank_in[r], (uintptr_t)rank_in[r] + span_bytes(M, H, ld.in, e)};
+    const Span res_span = {(uintptr_t)residual, (uintptr_t)residual + span_bytes(M, H, ld.res, e)};
+    ins[nin++] = {(uintptr_t)weight, (uintptr_t)weight + (uintptr_t)H * e};
     Span outs[4];
     int nout = 0;
-    const bool inplace = residual_out == residual;
-    outs[nout++] = {(uintptr_t)residual_out, (uintptr_t)residual_out + mat};
+    outs[nout++] = {(uintptr_t)residual_out, (uintptr_t)residual_out + span_bytes(M, H, ld.rout, e)};
     if (out)
-        outs[nout++] = {(uintptr_t)out, (uintptr_t)out + mat};
+        outs[nout++] = {(uintptr_t)out, (uintptr_t)out + span_bytes(M, H, ld.out, e)};
     if (fp8) {
-        outs[nout++] = {(uintptr_t)fp8_out, (uintptr_t)fp8_out + (uintptr_t)M * (uintptr_t)H};
+        outs[nout++] = {(uintptr_t)fp8_out, (uintptr_t)fp8_out + span_bytes(M, H, ld.q, 1)};
         outs[nout++] = {(uintptr_t)fp8_scale, (uintptr_t)fp8_scale + (uintptr_t)M * 4u};
     }
     for (int o = 0; o < nout; ++o) {
@@ -360,10 +389,10 @@ bool apply_shape(const ShapeReq *req, int P, int R, long long M, arrms::RowShape
 
 int fused_impl(const void *const *rank_in, int R, const void *residual, const void *weight,
                void *out, void *residual_out, void *fp8_out, float *fp8_scale, int M, int H,
-               float eps, int flags, const ShapeReq *req, hipStream_t stream)
+               float eps, int flags, const Strides &ld, const ShapeReq *req, hipStream_t stream)
 {
     int rc = validate(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H,
-                      eps, flags);
+                      eps, flags, ld);
     if (rc != ARRMS_OK)
         return rc;
     const int path = choose_path(M, H, R, flags);
@@ -385,6 +414,11 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
     a.fp8_scale = fp8 ? fp8_scale : nullptr;
     a.P = P;
     a.H = H;
+    a.ld_in = ld.in * e;
+    a.ld_res = ld.res * e;
+    a.ld_out = ld.out * e;
+    a.ld_rout = ld.rout * e;
+    a.ld_q = ld.q;
     a.eps = eps;
     a.gemma = (flags & ARRMS_GEMMA) != 0;
     a.exact_only = (flags & ARRMS_EXACT_ONLY) != 0;
@@ -432,22 +466,33 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
         return ARRMS_ERR_NO_STAGING;
     for (long long m0 = 0; m0 < M; m0 += chunk) {
         const long long n = (M - m0) < chunk ? (M - m0) : chunk;
-        const size_t off = (size_t)m0 * row_bytes;
         arrms::FlatArgs f;
         memset(&f, 0, sizeof(f));
         for (int r = 0; r < R; ++r)
-            f.in[r] = (const char *)rank_in[r] + off;
+            f.in[r] = (const char *)rank_in[r] + (size_t)m0 * (size_t)a.ld_in;
         f.dst = staging;
-        f.npacks = n * P;
+        // contiguous inputs reduce as one flat run of packs, strided ones row by row
+        if (ld.in == H) {
+            f.rows = 1;
+            f.P = n * P;
+        } else {
+            f.rows = n;
+            f.P = P;
+        }
+        f.ld_in = a.ld_in / 16;
+        f.ld_out = P;
+        f.tiles = (f.P + arrms::kFlatTile - 1) / arrms::kFlatTile;
+        f.nt_store = 0;  // the row pass reads the staging rows right away
         if (launch_flat(dt, f, R, stream) != hipSuccess)
             return ARRMS_ERR_HIP;
         arrms::RowArgs b = a;
         b.in[0] = staging;
-        b.residual = (const char *)residual + off;
-        b.residual_out = (char *)residual_out + off;
-        b.out = out ? (char *)out + off : nullptr;
+        b.ld_in = (long long)row_bytes;
+        b.residual = (const char *)residual + (size_t)m0 * (size_t)a.ld_res;
+        b.residual_out = (char *)residual_out + (size_t)m0 * (size_t)a.ld_rout;
+        b.out = out ? (char *)out + (size_t)m0 * (size_t)a.ld_out : nullptr;
         if (fp8) {
-            b.fp8_out = (char *)fp8_out + (size_t)m0 * (size_t)H;
+            b.fp8_out = (char *)fp8_out + (size_t)m0 * (size_t)a.ld_q;
             b.fp8_scale = fp8_scale + m0;
         }
         b.M = n;
@@ -471,8 +516,20 @@ int arrms_fused(const void *const *rank_in, int R, const void *residual, const v
                 void *out, void *residual_out, void *fp8_out, float *fp8_scale, int M, int H,
                 float eps, int flags, hipStream_t stream)
 {
+    const Strides ld = {H, H, H, H, H};
     return fused_impl(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H, eps,
-                      flags, nullptr, stream);
+                      flags, ld, nullptr, stream);
+}
+
+int arrms_fused_strided(const void *const *rank_in, int R, const void *residual, const void *weight,
+                        void *out, void *residual_out, void *fp8_out, float *fp8_scale, int M, int H,
+                        long long ld_in, long long ld_residual, long long ld_out,
+                        long long ld_residual_out, long long ld_fp8, float eps, int flags,
+                        hipStream_t stream)
+{
+    const Strides ld = {ld_in, ld_residual, ld_out, ld_residual_out, (flags & ARRMS_FP8) ? ld_fp8 : H};
+    return fused_impl(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H, eps,
+                      flags, ld, nullptr, stream);
 }
 
 int arrms_fused_config(const void *const *rank_in, int R, const void *residual, const void *weight,
@@ -483,8 +540,53 @@ int arrms_fused_config(const void *const *rank_in, int R, const void *residual, 
     if (ppt < 0 || tpr < 0 || rows_per_block < 0)
         return ARRMS_ERR_INVALID;
     const ShapeReq req = {ppt, tpr, rows_per_block};
+    const Strides ld = {H, H, H, H, H};
     return fused_impl(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H, eps,
-                      flags, &req, stream);
+                      flags, ld, &req, stream);
+}
+
+int arrms_allreduce_sum(const void *const *rank_in, int R, void *out, long long n, int flags,
+                        hipStream_t stream)
+{
+    if (flags & ~ARRMS_DTYPE_MASK)
+        return ARRMS_ERR_INVALID;
+    const int dt = flags & ARRMS_DTYPE_MASK;
+    if (dt > DT_FP32 || R < 1 || R > ARRMS_MAX_RANKS || n < 0 || !rank_in || !out)
+        return ARRMS_ERR_INVALID;
+    for (int r = 0; r < R; ++r)
+        if (!rank_in[r])
+            return ARRMS_ERR_INVALID;
+    const int e = esize(dt);
+    if ((n * e) % 16 != 0)
+        return ARRMS_ERR_UNSUPPORTED;
+    if (!aligned16(out))
+        return ARRMS_ERR_UNSUPPORTED;
+    for (int r = 0; r < R; ++r)
+        if (!aligned16(rank_in[r]))
+            return ARRMS_ERR_UNSUPPORTED;
+    if (n == 0)
+        return ARRMS_OK;
+    // the output may be one of the inputs exactly (in place), nothing else
+    const uintptr_t bytes = (uintptr_t)n * (uintptr_t)e;
+    const Span o = {(uintptr_t)out, (uintptr_t)out + bytes};
+    for (int r = 0; r < R; ++r) {
+        const Span i = {(uintptr_t)rank_in[r], (uintptr_t)rank_in[r] + bytes};
+        if (rank_in[r] != out && overlaps(o, i))
+            return ARRMS_ERR_INVALID;
+    }
+    arrms::FlatArgs f;
+    memset(&f, 0, sizeof(f));
+    for (int r = 0; r < R; ++r)
+        f.in[r] = rank_in[r];
+    f.dst = out;
+    f.rows = 1;
+    f.P = n * e / 16;
+    f.ld_in = f.P;
+    f.ld_out = f.P;
+    f.tiles = (f.P + arrms::kFlatTile - 1) / arrms::kFlatTile;
+    f.nt_store = 1;
+    (void)hipGetLastError();
+    return launch_flat(dt, f, R, stream) == hipSuccess ? ARRMS_OK : ARRMS_ERR_HIP;
 }
 
 }  // extern "C"

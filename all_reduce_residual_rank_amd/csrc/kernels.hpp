@@ -268,10 +268,11 @@ struct RowCtx {
 constexpr int kBufAuxNT = 2;               // cache policy: non-temporal
 constexpr int kBufDword3 = 0x00020000;     // 32-bit data format, raw (untyped) access
 
-ARRMS_DEV __amdgpu_buffer_rsrc_t row_rsrc(const void *base, long long row, int row_bytes)
+// Resource covering row_bytes bytes of the row that starts at base + row * ld.
+ARRMS_DEV __amdgpu_buffer_rsrc_t row_rsrc(const void *base, long long row, long long ld, int row_bytes)
 {
-    return __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)base + row * (long long)row_bytes),
-                                             (short)0, row_bytes, kBufDword3);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)base + row * ld), (short)0, row_bytes,
+                                             kBufDword3);
 }
 
 ARRMS_DEV u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off)
@@ -330,9 +331,9 @@ ARRMS_DEV void process_rows(const RowArgs &a, const RowCtx &c, long long g, cons
         __amdgpu_buffer_rsrc_t rs[R + 1];
 #pragma unroll
         for (int r = 0; r < R; ++r)
-            rs[r] = row_rsrc(a.in[r], row, rb);
-        rs[R] = row_rsrc(a.residual, row, rb);
-        const __amdgpu_buffer_rsrc_t rout = row_rsrc(a.residual_out, row, rb);
+            rs[r] = row_rsrc(a.in[r], row, a.ld_in, rb);
+        rs[R] = row_rsrc(a.residual, row, a.ld_res, rb);
+        const __amdgpu_buffer_rsrc_t rout = row_rsrc(a.residual_out, row, a.ld_rout, rb);
         constexpr int D = kPrefetch < PPT ? kPrefetch : PPT;
         u32x4 ring[D + 1][R + 1];
 #pragma unroll
@@ -422,8 +423,8 @@ ARRMS_DEV void process_rows(const RowArgs &a, const RowCtx &c, long long g, cons
         if (c.lt == 0)
             a.fp8_scale[row] = scale;
     }
-    const __amdgpu_buffer_rsrc_t rout_t = row_rsrc(a.out, row, rb);
-    const __amdgpu_buffer_rsrc_t rout_q = row_rsrc(a.fp8_out, row, rb / 2);
+    const __amdgpu_buffer_rsrc_t rout_t = row_rsrc(a.out, row, a.ld_out, rb);
+    const __amdgpu_buffer_rsrc_t rout_q = row_rsrc(a.fp8_out, row, a.ld_q, rb / 2);
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
         const uint32_t off = (uint32_t)(c.lt + k * c.tpr) * 16u;
@@ -554,13 +555,18 @@ __global__ void __launch_bounds__(512) row_kernel(const RowArgs a)
 }
 
 // --------------------------------------------------------------------------
-// Flat rank reduce (stage 1 of two-stage, PR #3462 Technical Details): every
-// thread reduces whole packs across the R inputs in rank order in fp32,
-// rounds to T and writes the staging buffer. No LDS, no barrier. Tiles are
-// kFlatTile packs; only the last block of a TAIL grid checks bounds.
-template <int DT, int R>
-ARRMS_DEV void flat_packs(const FlatArgs &a, const long long (&j)[kFlatPacksPerThread],
-                          const bool (&ok)[kFlatPacksPerThread])
+// Flat rank reduce (stage 1 of two-stage, PR #3462 Technical Details; and the
+// sum-only rank all-reduce): every thread reduces whole packs across the R
+// inputs in rank order in fp32, rounds to T and writes the destination. No
+// LDS, no barrier. Block b takes tile b % tiles of row b / tiles; a tile is
+// kFlatTile packs. TAIL=false is the aligned variant (P a multiple of the
+// tile): no bounds checks. With TAIL only the last tile of a row checks its
+// bounds, and every thread still runs the same code path (PR #5807 Proposed
+// modifications: complete tiles unpredicated, leftover packs reduced by their
+// owner threads).
+template <int DT, int R, bool NTS>
+ARRMS_DEV void flat_packs(const FlatArgs &a, long long src_row, long long dst_row,
+                          const long long (&j)[kFlatPacksPerThread], const bool (&ok)[kFlatPacksPerThread])
 {
     using F = Fmt<DT>;
     constexpr int EPW = F::EPW;
@@ -570,7 +576,7 @@ ARRMS_DEV void flat_packs(const FlatArgs &a, const long long (&j)[kFlatPacksPerT
         if (ok[k]) {
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                xv[r][k] = ld16_nt(a.in[r], j[k]);
+                xv[r][k] = ld16_nt(a.in[r], src_row + j[k]);
         }
 #pragma unroll
     for (int k = 0; k < kFlatPacksPerThread; ++k) {
@@ -591,23 +597,29 @@ ARRMS_DEV void flat_packs(const FlatArgs &a, const long long (&j)[kFlatPacksPerT
             }
             out[i] = F::pack(acc);
         }
-        st16(a.dst, j[k], out);
+        if constexpr (NTS)
+            st16_nt(a.dst, dst_row + j[k], out);
+        else
+            st16(a.dst, dst_row + j[k], out);
     }
 }
 
-template <int DT, int R, bool TAIL>
+template <int DT, int R, bool TAIL, bool NTS>
 __global__ void __launch_bounds__(kFlatThreads) flat_kernel(const FlatArgs a)
 {
-    const long long base = (long long)blockIdx.x * kFlatTile + threadIdx.x;
+    const long long b = blockIdx.x;
+    const long long row = b / a.tiles;  // scalar: one division per block
+    const long long tile = b - row * a.tiles;
+    const long long base = tile * kFlatTile + threadIdx.x;
     long long j[kFlatPacksPerThread];
     bool ok[kFlatPacksPerThread];
-    const bool last = TAIL && blockIdx.x == gridDim.x - 1;
+    const bool last = TAIL && tile == a.tiles - 1;
 #pragma unroll
     for (int k = 0; k < kFlatPacksPerThread; ++k) {
         j[k] = base + (long long)k * kFlatThreads;
-        ok[k] = !last || j[k] < a.npacks;
+        ok[k] = !last || j[k] < a.P;
     }
-    flat_packs<DT, R>(a, j, ok);
+    flat_packs<DT, R, NTS>(a, row * a.ld_in, row * a.ld_out, j, ok);
 }
 
 // --------------------------------------------------------------------------
@@ -655,13 +667,24 @@ static hipError_t row_launch_epi(const RowArgs &a, int R, const RowShape &s, hip
 template <int DT, int R>
 static hipError_t flat_go(const FlatArgs &a, hipStream_t st)
 {
-    const long long tiles = (a.npacks + kFlatTile - 1) / kFlatTile;
-    const bool tail = a.npacks % kFlatTile != 0;
-    dim3 grid((unsigned)tiles), block(kFlatThreads);
-    if (tail)
-        hipLaunchKernelGGL((flat_kernel<DT, R, true>), grid, block, 0, st, a);
-    else
-        hipLaunchKernelGGL((flat_kernel<DT, R, false>), grid, block, 0, st, a);
+    const long long blocks = a.rows * a.tiles;
+    if (blocks <= 0)
+        return hipSuccess;
+    if (blocks > 0x7fffffffLL)
+        return hipErrorInvalidValue;
+    const bool tail = a.P % kFlatTile != 0;
+    dim3 grid((unsigned)blocks), block(kFlatThreads);
+    if (a.nt_store) {
+        if (tail)
+            hipLaunchKernelGGL((flat_kernel<DT, R, true, true>), grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL((flat_kernel<DT, R, false, true>), grid, block, 0, st, a);
+    } else {
+        if (tail)
+            hipLaunchKernelGGL((flat_kernel<DT, R, true, false>), grid, block, 0, st, a);
+        else
+            hipLaunchKernelGGL((flat_kernel<DT, R, false, false>), grid, block, 0, st, a);
+    }
     return hipGetLastError();
 }
 

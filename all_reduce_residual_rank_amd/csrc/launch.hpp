@@ -25,6 +25,8 @@ struct RowArgs {
     float *fp8_scale;     // [M]
     long long M;          // rows
     int P;                // 16-byte packs per row
+    // row strides in bytes: rank inputs, residual, out, residual_out, fp8 codes
+    long long ld_in, ld_res, ld_out, ld_rout, ld_q;
     int H;                // elements per row
     int tpr;              // threads per row group (multiple of 64)
     float eps;
@@ -33,10 +35,18 @@ struct RowArgs {
 };
 
 // Arguments of the flat rank reduce (stage 1 of two-stage).
+// The reduced region is rows x P packs: row m of rank r starts at pack
+// m * ld_in of in[r] and lands at pack m * ld_out of dst. Contiguous data is
+// one row of all its packs.
 struct FlatArgs {
     const void *in[kMaxRanks];
     void *dst;
-    long long npacks;     // packs to reduce
+    long long rows;
+    long long P;          // packs per row
+    long long ld_in;      // row stride of the inputs, in packs
+    long long ld_out;     // row stride of dst, in packs
+    long long tiles;      // tiles per row (ceil(P / kFlatTile))
+    int nt_store;         // non-temporal stores (the result is not read back soon)
 };
 
 // Row kernel shape: PPT packs per thread per row, tpr threads per row,

@@ -96,3 +96,57 @@ TAIL_FP32 = Workload("r4_m1025_h512_fp32", R=4, M=1025, H=512, dtype="fp32")
 
 ALL = [SMALL, HEADLINE, FP8_GEMMA, WIDE_R8, *TAILS, TAIL_FP32]
 BY_NAME = {w.name: w for w in ALL}
+
+
+# ---- the plain rank all-reduce (no norm epilogue) ---------------------------
+# Message sizes of the flattened sweep in ROCm/aiter PR #5807 (benchmark case
+# sets): representative byte sizes, the 1 MiB tile boundary and its
+# neighbours (+-64 B, 63/64/65 packs-of-64 B), the (M, 2880) upstream rows and
+# the (1023/1024/1025, 512) regression rows. Sizes that give an element count
+# already listed are dropped, as the sweep does.
+SUM_BYTES = (8192, 65536, 262144, 524288, 1048576, 4194304, 8388608)
+SUM_TILE_OFFSETS = (-64, 0, 64, 63 * 64, 64 * 64, 65 * 64)
+SUM_UPSTREAM_M = (120, 121, 127, 157, 160, 161, 256, 512)
+SUM_REGRESSION_M = (1023, 1024, 1025)
+
+
+@dataclass(frozen=True)
+class SumCase:
+    name: str
+    dtype: str
+    numel: int
+
+    @property
+    def esize(self) -> int:
+        return 4 if self.dtype == "fp32" else 2
+
+    @property
+    def nbytes(self) -> int:
+        return self.numel * self.esize
+
+
+def sum_cases(dtype: str) -> list[SumCase]:
+    e = 4 if dtype == "fp32" else 2
+    cand = [(f"shape_{m}x512", m * 512) for m in SUM_REGRESSION_M]
+    cand += [(f"bytes_{n}", n // e) for n in SUM_BYTES]
+    cand += [(f"tile_boundary_{o:+d}", (1048576 + o) // e) for o in SUM_TILE_OFFSETS]
+    cand += [(f"upstream_{m}x2880", m * 2880) for m in SUM_UPSTREAM_M]
+    seen, cases = set(), []
+    for name, numel in cand:
+        if numel in seen:
+            continue
+        seen.add(numel)
+        cases.append(SumCase(name, dtype, numel))
+    return cases
+
+
+def make_sum_inputs(R: int, numel: int, seed: int, dtype: str = "bf16", sigma: float = 1.0):
+    """R rank tensors of numel elements, N(0, sigma) cast to T (RNE)."""
+    g = torch.Generator().manual_seed(seed)
+    T = DTYPES[dtype]
+    return [(torch.randn(numel, generator=g) * sigma).to(T) for _ in range(R)]
+
+
+# The sum-only benchmark message: the rank inputs of the prefill rows
+# (R=4, 1024 x 6144 bf16, 12 MiB per rank).
+SUM_HEADLINE = SumCase("sum_r4_n6291456_bf16", "bf16", 1024 * 6144)

@@ -112,6 +112,55 @@ ARRMS_API int arrms_fused(const void *const *rank_in, int R, const void *residua
                 float eps, int flags, hipStream_t stream);
 
 /*
+ * arrms_fused_strided -- arrms_fused over row-strided (padded) matrices. The
+ * pages' communicator declines padded or strided rows and falls back to its
+ * unfused path (PR #6699 Changes); this entry point takes them fused.
+ *
+ * Row m of rank input r starts at element m * ld_in of rank_in[r]; likewise
+ * ld_residual, ld_out and ld_residual_out for residual, out and residual_out,
+ * all counted in elements of T, and ld_fp8 for fp8_out, counted in bytes
+ * (ignored without ARRMS_FP8). Only the first H elements of each row are read
+ * or written: the padding between rows is never touched. Every stride is at
+ * least H (else ARRMS_ERR_INVALID) and spans a multiple of 16 bytes, ld_fp8 a
+ * multiple of 8 bytes (else ARRMS_ERR_UNSUPPORTED). In place (residual_out == residual) requires
+ * ld_residual_out == ld_residual. Overlap is judged on each matrix's whole
+ * byte range, first element to last, padding included. Everything else --
+ * arguments, results, paths, staging and error behaviour -- is arrms_fused's;
+ * with every stride equal to H the call is arrms_fused.
+ */
+ARRMS_API int arrms_fused_strided(const void *const *rank_in, int R, const void *residual,
+                                  const void *weight, void *out, void *residual_out, void *fp8_out,
+                                  float *fp8_scale, int M, int H, long long ld_in,
+                                  long long ld_residual, long long ld_out, long long ld_residual_out,
+                                  long long ld_fp8, float eps, int flags, hipStream_t stream);
+
+/*
+ * arrms_allreduce_sum -- the plain rank all-reduce without the norm epilogue
+ * (the flattened message sweep of PR #5807 Proposed modifications, and the
+ * rank-ordered reduce of PR #3462 Technical Details): for every element
+ * i < n, out[i] = RNE_T(x_0[i] + x_1[i] + ... + x_{R-1}[i]) with fp32 adds in
+ * rank order 0..R-1 and the accumulator starting at x_0 (for T = fp32 the
+ * fp32 sum itself).
+ *
+ * rank_in  host array of R device pointers, each to n elements of T (read
+ *          during the call, as in arrms_fused). Rank pointers may repeat.
+ * R        1 .. ARRMS_MAX_RANKS.
+ * out      device n elements of T; may equal one of the rank pointers
+ *          exactly (in place), must not overlap any of them otherwise.
+ * n        elements, >= 0 (0: returns ARRMS_OK, launches nothing), with
+ *          n * sizeof(T) % 16 == 0 (else ARRMS_ERR_UNSUPPORTED).
+ * flags    ARRMS_DTYPE_* only; any other bit gives ARRMS_ERR_INVALID.
+ * stream   HIP stream; one kernel launch, asynchronous, no allocation, no
+ *          shared state (safe in graph capture and on concurrent streams).
+ *
+ * Every device pointer must be 16-byte aligned (else ARRMS_ERR_UNSUPPORTED).
+ * Complete 512-pack tiles run without bounds checks; only the last tile of a
+ * ragged message checks them (PR #5807 Proposed modifications, has_tail).
+ */
+ARRMS_API int arrms_allreduce_sum(const void *const *rank_in, int R, void *out, long long n, int flags,
+                                  hipStream_t stream);
+
+/*
  * arrms_fused_config -- arrms_fused with an explicit launch shape for the row
  * kernel, for benchmarking and tuning (the automatic choice is the shape
  * arrms_fused takes). ppt: 16-byte packs per thread and row (1, 2 or 4); tpr:

@@ -56,6 +56,8 @@ def _load():
     lib.oracle_fused_rows.restype = i
     lib.oracle_quant_rows.argtypes = [vp, i, i, i, vp, vp]
     lib.oracle_quant_rows.restype = i
+    lib.oracle_rank_sum.argtypes = [ctypes.POINTER(vp), i, vp, ctypes.c_size_t, i]
+    lib.oracle_rank_sum.restype = i
     sz = ctypes.c_size_t
     for name in ("orc_bf16_from_double_n", "orc_fp16_from_double_n", "orc_e4m3_from_float_n"):
         getattr(lib, name).argtypes = [vp, vp, sz]
@@ -108,6 +110,23 @@ def fused(xs, residual, weight, eps: float, flags: int, *, want_out: bool = True
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (rc={rc})")
     return {"out": out, "residual_out": res_out, "fp8": q, "scale": sc}
+
+
+def rank_sum(xs, dt: int) -> np.ndarray:
+    """Step O1 alone: the rank-ordered sum of the R arrays (storage bits of T,
+    any equal shapes), rounded to T. Returns an array of the same shape."""
+    lib = _load()
+    sdt = storage_dtype(dt)
+    xs = [np.ascontiguousarray(x, dtype=sdt) for x in xs]
+    shape = xs[0].shape
+    for x in xs:
+        assert x.shape == shape
+    out = np.zeros(shape, dtype=sdt)
+    ptrs = (ctypes.c_void_p * len(xs))(*[x.ctypes.data for x in xs])
+    rc = lib.oracle_rank_sum(ptrs, len(xs), _ptr(out), int(out.size), int(dt))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (rc={rc})")
+    return out
 
 
 def quant(y: np.ndarray, dt: int):

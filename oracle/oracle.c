@@ -288,6 +288,24 @@ int oracle_fused_rows(const void *const *rank_in, int R, const void *residual,
     return 0;
 }
 
+/* Step O1 alone over n elements: the plain rank all-reduce (the flattened
+ * message sweep of PR #5807 "Specialize partial tiles in two-stage custom
+ * all-reduce", section Proposed modifications; the rank order of PR #3462
+ * Technical Details). out may be one of the inputs. Returns 0, or -1 for an
+ * argument this oracle does not define. */
+int oracle_rank_sum(const void *const *rank_in, int R, void *out, size_t n, int dt)
+{
+    if (R < 1 || dt < 0 || dt > ORC_DT_FP32)
+        return -1;
+    for (size_t i = 0; i < n; ++i) {
+        float acc = load_t(rank_in[0], i, dt);
+        for (int r = 1; r < R; ++r)
+            acc = acc + load_t(rank_in[r], i, dt);
+        store_t(out, i, round_t((double)acc, dt), dt);
+    }
+    return 0;
+}
+
 /* Quantisation step O5 alone, applied to given T rows (used to check the
  * FP8 bytes of a result against its own T mirror and scale). */
 int oracle_quant_rows(const void *y_in, int dt, int M, int H, uint8_t *q_out,

@@ -131,3 +131,70 @@ def test_query_path():
     assert arrms.arrms_query_path(1024, 60, 4, 0) == arrms.ERR_UNSUPPORTED
     assert arrms.arrms_query_path(1024, 64, 9, 0) == arrms.ERR_INVALID
     assert arrms.arrms_query_path(16, 512, 4, arrms.DTYPE_FP32 | arrms.FP8) == arrms.ERR_UNSUPPORTED
+
+
+def _call_strided(R=4, M=8, H=64, flags=0, eps=1e-6, ld=(64, 64, 64, 64, 64), **over):
+    ptr = {f"in{r}": BASE + r * STRIDE for r in range(8)}
+    ptr.update(residual=BASE + 10 * STRIDE, weight=BASE + 11 * STRIDE, out=BASE + 12 * STRIDE,
+               residual_out=BASE + 13 * STRIDE, fp8_out=BASE + 14 * STRIDE,
+               fp8_scale=BASE + 15 * STRIDE)
+    ptr.update(over)
+    rank_in = [ptr[f"in{r}"] for r in range(R)]
+    return arrms.arrms_fused_strided_raw(rank_in, R, ptr["residual"], ptr["weight"], ptr["out"],
+                                         ptr["residual_out"], ptr["fp8_out"], ptr["fp8_scale"], M, H,
+                                         *ld, eps, flags, None)
+
+
+def test_strided_argument_checks():
+    assert _call_strided(M=0) == arrms.OK
+    assert _call_strided(M=0, ld=(72, 80, 64, 96, 64)) == arrms.OK
+    # a stride below the row is invalid, one that breaks 16-byte rows unsupported
+    for i in range(4):
+        ld = [64] * 5
+        ld[i] = 56
+        assert _call_strided(ld=tuple(ld)) == arrms.ERR_INVALID
+        ld[i] = 68                                 # 136-byte bf16 rows
+        assert _call_strided(ld=tuple(ld)) == arrms.ERR_UNSUPPORTED
+    # fp8 stride counts bytes: >= H and a multiple of 8
+    assert _call_strided(flags=arrms.FP8, ld=(64, 64, 64, 64, 48)) == arrms.ERR_INVALID
+    assert _call_strided(flags=arrms.FP8, ld=(64, 64, 64, 64, 68)) == arrms.ERR_UNSUPPORTED
+    assert _call_strided(M=0, flags=arrms.FP8, ld=(64, 64, 64, 64, 72)) == arrms.OK
+    # FP8 with 8-byte code rows (H = 8) at unit stride
+    assert _call_strided(M=0, H=8, flags=arrms.FP8, ld=(8, 8, 8, 8, 8)) == arrms.OK
+    assert _call(M=0, H=8, flags=arrms.FP8) == arrms.OK
+    # without FP8 the fp8 stride is ignored
+    assert _call_strided(M=0, ld=(64, 64, 64, 64, 0)) == arrms.OK
+    # fp32 rows: 4-element multiples
+    assert _call_strided(flags=arrms.DTYPE_FP32, ld=(66, 64, 64, 64, 64)) == arrms.ERR_UNSUPPORTED
+    assert _call_strided(M=0, flags=arrms.DTYPE_FP32, ld=(68, 64, 64, 64, 64)) == arrms.OK
+    # in place needs equal residual strides
+    assert _call_strided(residual_out=BASE + 10 * STRIDE, ld=(64, 64, 64, 80, 64)) == arrms.ERR_INVALID
+    assert _call_strided(M=0, residual_out=BASE + 10 * STRIDE, ld=(64, 80, 64, 80, 64)) == arrms.OK
+
+
+def test_strided_overlap_counts_the_padding():
+    M, H, ld = 8, 64, 128
+    span = ((M - 1) * ld + H) * 2
+    lds = (ld, ld, ld, ld, ld)
+    # out placed inside the padded span of residual_out overlaps it
+    assert _call_strided(ld=lds, out=BASE + 13 * STRIDE + span - 16) == arrms.ERR_INVALID
+    # ... and just past the span it does not (M = 0 stops before any launch)
+    assert _call_strided(M=0, ld=lds, out=BASE + 13 * STRIDE + span) == arrms.OK
+
+
+def _sum(R=4, n=4096, flags=0, out=BASE + 12 * STRIDE, **over):
+    ptr = {f"in{r}": BASE + r * STRIDE for r in range(9)}
+    ptr.update(over)
+    return arrms.arrms_allreduce_sum_raw([ptr[f"in{r}"] for r in range(R)], R, out, n, flags, None)
+
+
+def test_allreduce_sum_argument_checks():
+    assert _sum(n=0) == arrms.OK
+    assert _sum(n=0, out=BASE) == arrms.OK                   # in place on rank 0
+    for kw in (dict(R=0), dict(R=9), dict(n=-8), dict(flags=3), dict(flags=arrms.GEMMA),
+               dict(flags=arrms.FP8), dict(flags=arrms.FORCE_TWO_STAGE), dict(out=None),
+               dict(in1=None), dict(out=BASE + STRIDE + 16)):
+        assert _sum(**kw) == arrms.ERR_INVALID, kw
+    for kw in (dict(n=4100), dict(n=2050, flags=arrms.DTYPE_FP32), dict(out=BASE + 12 * STRIDE + 8),
+               dict(in3=BASE + 3 * STRIDE + 4)):
+        assert _sum(**kw) == arrms.ERR_UNSUPPORTED, kw
