@@ -13,6 +13,9 @@ Prints one JSON line:
               residual read, out and residual_out written, the weight) over the
               measured kernel duration, against MI355X's 8 TB/s HBM peak
   cpu_baseline  the CPU oracle, single-threaded, on the same workload
+  allreduce_sum the plain rank all-reduce (no norm) over a message of the same
+              rank inputs' size (4 x 1024 x 6144 bf16), with its own roofline
+              fraction; --sum-only prints that measurement as the line instead
 """
 from __future__ import annotations
 
@@ -45,6 +48,10 @@ def parse():
                    help="bound on the CPU-baseline work")
     p.add_argument("--no-other-path", action="store_true", help="time only the chosen path")
     p.add_argument("--no-hot", action="store_true", help="skip the cache-resident context number")
+    p.add_argument("--no-sum", action="store_true",
+                   help="skip the plain rank all-reduce (no norm) timing")
+    p.add_argument("--sum-only", action="store_true",
+                   help="time only the plain rank all-reduce (R=4, 1024 x 6144 bf16 message)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 256 MiB device-to-device copy (4 times) so that a "
                         "profiler's FETCH_SIZE/WRITE_SIZE can be scaled by a kernel of known size")
@@ -99,19 +106,20 @@ def call(arrms, wl, d, flags, stream):
                       flags=flags, M=wl.M, H=wl.H, stream=stream)
 
 
-def time_path(torch, arrms, wl, sets, flags, steps, warmup):
-    """Warm up, then time exactly `steps` calls replayed from one HIP graph."""
+def time_graph(torch, calls, steps, warmup):
+    """Warm up, then time exactly `steps` calls replayed from one HIP graph.
+    calls: functions f(stream) that each enqueue one call; used in turn."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
-    n = len(sets.sets)
+    n = len(calls)
     gw = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gw, stream=s):
         for i in range(warmup):
-            call(arrms, wl, sets.sets[i % n], flags, s)
+            calls[i % n](s)
     gk = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gk, stream=s):
         for i in range(steps):
-            call(arrms, wl, sets.sets[i % n], flags, s)
+            calls[i % n](s)
     torch.cuda.synchronize()
     with torch.cuda.stream(s):
         gw.replay()
@@ -126,6 +134,27 @@ def time_path(torch, arrms, wl, sets, flags, steps, warmup):
     ms = e0.elapsed_time(e1)
     del gw, gk
     return ms
+
+
+def time_path(torch, arrms, wl, sets, flags, steps, warmup):
+    calls = [lambda st, d=d: call(arrms, wl, d, flags, st) for d in sets.sets]
+    return time_graph(torch, calls, steps, warmup)
+
+
+def time_sum(torch, arrms, case, R, steps, warmup):
+    """The plain rank all-reduce on one message over rotating buffer sets.
+    Returns (us per call, algorithmic bytes per call)."""
+    from all_reduce_residual_rank_amd import workloads as wlmod
+    dev = torch.device("cuda")
+    xs = wlmod.make_sum_inputs(R, case.numel, 0, case.dtype)
+    nsets = max(2, -(-ROTATE_BYTES // ((R + 1) * case.nbytes)))
+    sets = [([x.to(dev) for x in xs], torch.empty(case.numel, dtype=wlmod.DTYPES[case.dtype], device=dev))
+            for _ in range(nsets)]
+    flags = wlmod.DT_CODE[case.dtype]
+    calls = [lambda st, d=d: arrms.arrms_allreduce_sum(d[0], d[1], flags=flags, stream=st) for d in sets]
+    ms = time_graph(torch, calls, steps, warmup)
+    del sets
+    return ms * 1000.0 / steps, (R + 1) * case.nbytes
 
 
 def time_hot(torch, arrms, wl, sets, flags, reps=64):
@@ -206,6 +235,24 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.sum_only:
+        case = wlmod.SUM_HEADLINE
+        us, nbytes = time_sum(torch, arrms, case, 4, args.steps, args.warmup)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        digest = sources_digest()
+        print(json.dumps({
+            "metric": "µs/call and achieved HBM GB/s of the plain rank all-reduce, R=4",
+            "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(us / 1000.0, 6), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": case.dtype, "data": "synthetic",
+            "config": {"workload": case.name, "R": 4, "numel": case.numel},
+            "us_per_call": round(us, 3),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_GBS, 4),
+                         "traffic": load_traffic(case.name, "flat", digest),
+                         "algorithmic_bytes": nbytes, "kernel": "flat_kernel"},
+            "sources_digest": digest}), flush=True)
+        return
     e = wl.esize
     set_bytes = (wl.R + 3) * wl.M * wl.H * e
     nsets = max(2, -(-ROTATE_BYTES // set_bytes))
@@ -256,6 +303,15 @@ def main():
         "device": torch.cuda.get_device_name(0),
         "arch": torch.cuda.get_device_properties(0).gcnArchName,
     }
+    if not args.no_sum:
+        # the plain rank all-reduce (no norm) on the same rank inputs' size
+        case = wlmod.SUM_HEADLINE
+        sum_us, sum_bytes = time_sum(torch, arrms, case, 4, args.steps, args.warmup)
+        line["allreduce_sum"] = {"message": case.name, "R": 4, "us_per_call": round(sum_us, 3),
+                                 "achieved": round(sum_bytes / (sum_us * 1e-6) / 1e9, 2),
+                                 "unit": "GB/s", "algorithmic_bytes": sum_bytes,
+                                 "frac": round(sum_bytes / (sum_us * 1e-6) / 1e9 / PEAK_GBS, 4),
+                                 "kernel": "flat_kernel"}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)
