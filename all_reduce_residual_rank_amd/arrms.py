@@ -57,7 +57,7 @@ _lib.arrms_fused_strided.restype = _i
 _lib.arrms_allreduce_sum.argtypes = [ctypes.POINTER(_vp), _i, _vp, _ll, _i, _vp]
 _lib.arrms_allreduce_sum.restype = _i
 _lib.arrms_fused_config.argtypes = [ctypes.POINTER(_vp), _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i,
-                                    _i, _i, _i, _vp]
+                                    _i, _i, _i, _i, _i, _vp]
 _lib.arrms_fused_config.restype = _i
 _lib.arrms_reserve_staging.argtypes = [_sz]
 _lib.arrms_reserve_staging.restype = _i
@@ -110,24 +110,26 @@ def arrms_fused_raw(rank_in, R, residual, weight, out, residual_out, fp8_out, fp
 
 
 def arrms_fused_config_raw(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale,
-                           M, H, eps, flags, ppt, tpr, rows_per_block, stream) -> int:
+                           M, H, eps, flags, ppt, tpr, rows_per_block, blocks, stream,
+                           load_window=0) -> int:
     """arrms_fused_config with addresses as ints; returns the status unchanged."""
     ptrs = (_vp * max(len(rank_in), 1))(*[_addr(p) for p in rank_in])
     return _lib.arrms_fused_config(ptrs, int(R), _addr(residual), _addr(weight), _addr(out),
                                    _addr(residual_out), _addr(fp8_out), _addr(fp8_scale), int(M),
                                    int(H), float(eps), int(flags), int(ppt), int(tpr),
-                                   int(rows_per_block), stream)
+                                   int(rows_per_block), int(blocks), int(load_window), stream)
 
 
 def arrms_fused_config(rank_in, residual, weight, out, residual_out, fp8_out=None, fp8_scale=None, *,
                        eps: float, flags: int, ppt: int = 0, tpr: int = 0, rows_per_block: int = 0,
-                       M: int | None = None, H: int | None = None, stream=None) -> None:
+                       blocks: int = 0, load_window: int = 0, M: int | None = None,
+                       H: int | None = None, stream=None) -> None:
     """arrms_fused with an explicit row-kernel launch shape (0 = automatic)."""
     if M is None or H is None:
         M, H = residual.shape[-2], residual.shape[-1]
     rc = arrms_fused_config_raw(rank_in, len(rank_in), residual, weight, out, residual_out, fp8_out,
-                                fp8_scale, M, H, eps, flags, ppt, tpr, rows_per_block,
-                                _stream_handle(stream))
+                                fp8_scale, M, H, eps, flags, ppt, tpr, rows_per_block, blocks,
+                                _stream_handle(stream), load_window=load_window)
     if rc != OK:
         raise ArrmsError(rc, "arrms_fused_config")
 

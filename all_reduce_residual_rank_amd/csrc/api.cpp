@@ -185,7 +185,7 @@ int choose_path(int M, int H, int R, int flags)
 arrms::RowShape choose_shape(int P, int R, long long M, bool fp8)
 {
     (void)M;
-    arrms::RowShape best = {0, 0, 0, false};
+    arrms::RowShape best = {0, 0, 0, false, 0, 0};
     long long best_key = -1;
     const int ppts[3] = {1, 2, 4};
     for (int c = 0; c < 3; ++c) {
@@ -202,7 +202,7 @@ arrms::RowShape choose_shape(int P, int R, long long M, bool fp8)
         const long long key = (long long)waste * 16 + (4 - ppt);
         if (best_key < 0 || key < best_key) {
             best_key = key;
-            best = {ppt, tpr, 1, waste != 0};
+            best = {ppt, tpr, 1, waste != 0, 0, 0};
         }
     }
     if (best.ppt == 0) {
@@ -211,7 +211,7 @@ arrms::RowShape choose_shape(int P, int R, long long M, bool fp8)
             int tpr = (P + ppts[c] - 1) / ppts[c];
             tpr = (tpr + 63) / 64 * 64;
             if (tpr <= 512)
-                best = {ppts[c], tpr, 1, tpr * ppts[c] != P};
+                best = {ppts[c], tpr, 1, tpr * ppts[c] != P, 0, 0};
         }
     }
     if (best.ppt == 0)
@@ -355,7 +355,7 @@ size_t arrms_staging_bytes(void)
 namespace {
 
 struct ShapeReq {
-    int ppt, tpr, rpb;  // 0 = automatic
+    int ppt, tpr, rpb, grid, window;  // 0 = automatic
 };
 
 // Apply an explicit shape request on top of the automatic choice; returns
@@ -378,12 +378,18 @@ bool apply_shape(const ShapeReq *req, int P, int R, long long M, arrms::RowShape
             return false;
         s.tpr = req->tpr;
     }
-    if ((long long)s.tpr * s.ppt < P || s.tpr > 512)
+    // blocks of one pack per thread may hold 1024 threads, others 512
+    const int max_block = s.ppt == 1 ? 1024 : 512;
+    if ((long long)s.tpr * s.ppt < P || s.tpr > max_block)
         return false;
     s.tail = s.tpr * s.ppt != P;
     s.rpb = req->rpb ? req->rpb : (s.tpr >= 256 ? 1 : 256 / s.tpr);
-    if (s.rpb < 1 || s.tpr * s.rpb > 512)
+    if (s.rpb < 1 || s.tpr * s.rpb > max_block)
         return false;
+    s.grid = req->grid;
+    if (req->window < 0 || req->window > 2)
+        return false;
+    s.window = req->window;
     return true;
 }
 
@@ -534,12 +540,12 @@ int arrms_fused_strided(const void *const *rank_in, int R, const void *residual,
 
 int arrms_fused_config(const void *const *rank_in, int R, const void *residual, const void *weight,
                        void *out, void *residual_out, void *fp8_out, float *fp8_scale, int M, int H,
-                       float eps, int flags, int ppt, int tpr, int rows_per_block,
-                       hipStream_t stream)
+                       float eps, int flags, int ppt, int tpr, int rows_per_block, int blocks,
+                       int load_window, hipStream_t stream)
 {
-    if (ppt < 0 || tpr < 0 || rows_per_block < 0)
+    if (ppt < 0 || tpr < 0 || rows_per_block < 0 || blocks < 0 || load_window < 0 || load_window > 2)
         return ARRMS_ERR_INVALID;
-    const ShapeReq req = {ppt, tpr, rows_per_block};
+    const ShapeReq req = {ppt, tpr, rows_per_block, blocks, load_window};
     const Strides ld = {H, H, H, H, H};
     return fused_impl(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H, eps,
                       flags, ld, &req, stream);

@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "launch.hpp"
 
 namespace arrms {
@@ -290,246 +292,324 @@ ARRMS_DEV void bstore8(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
     __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kBufAuxNT);
 }
 
-// Phase 1 streams through the thread's packs with a prefetch distance of
-// kPrefetch packs: the loads of pack k + kPrefetch (all R inputs and the
-// residual) are issued before pack k is reduced. A handful of 16-byte loads
-// in flight per wave keeps HBM busy across the resident blocks; issuing all of
-// a row's loads at once measured slower on MI355X and costs registers.
-constexpr int kPrefetch = 1;
+// Phase 1 keeps at most W 16-byte loads of a thread in flight (a sliding
+// window over the row's loads, pack by pack, input streams in rank order).
+// HBM on MI355X delivers the most when roughly 6-9 MB are outstanding across
+// the device. When every row of a large launch is resident at once, a window
+// of kWindowLow loads per thread is that amount (more measured slower: the
+// DRAM pages of the many streams get interleaved; fewer starve the memory
+// pipeline). Launches that run in several rounds of blocks, or that are
+// small, do better with the wide window (the whole row, up to kWindowHigh
+// loads), which hides each block's latency.
+constexpr int kWindowLow = 3;
+constexpr int kWindowHigh = 16;
 
-template <int R>
-ARRMS_DEV void load_pack(const __amdgpu_buffer_rsrc_t (&rs)[R + 1], uint32_t off, u32x4 (&x)[R + 1])
+template <int N> ARRMS_DEV void wait_vm()
 {
-#pragma unroll
-    for (int r = 0; r <= R; ++r)
-        x[r] = bload(rs[r], off);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int DT, int R, int PPT, int EPI>
-ARRMS_DEV void process_rows(const RowArgs &a, const RowCtx &c, long long g, const u32x4 (&wv)[PPT],
-                            double (&red)[2][kMaxWavesPerBlock][2], int &parity)
+// Buffer resources of one row's streams: the inputs (R rank inputs, then the
+// residual) and the outputs (residual_out, the T output, the FP8 codes). A
+// row past M gets empty resources: its loads return zero and its stores are
+// dropped, so idle row slots run the same code as real rows.
+template <int R>
+ARRMS_DEV void in_streams(const RowArgs &a, long long row, int rb, __amdgpu_buffer_rsrc_t (&s)[R + 1])
+{
+    const int n = row < a.M ? rb : 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        s[r] = row_rsrc(a.in[r], row, a.ld_in, n);
+    s[R] = row_rsrc(a.residual, row, a.ld_res, n);
+}
+
+// Output resource of a row (rows past M: empty); bytes = the row's bytes in
+// that output.
+ARRMS_DEV __amdgpu_buffer_rsrc_t out_stream(const void *base, long long row, long long ld, int bytes,
+                                            long long M)
+{
+    return row_rsrc(base, row, ld, row < M ? bytes : 0);
+}
+
+// Phase-1 arithmetic of one pack: rank sum in fp32, RNE to T, residual add,
+// RNE to T (h), exact squares of h into fp64 partial sums, and for FP8 the
+// running max of |h * w_eff|.
+template <int DT, int R, bool FP8>
+ARRMS_DEV void reduce_pack(const u32x4 (&x)[R + 1], const u32x4 &w, double gadd, u32x4 &hv,
+                           double (&ssw)[4], double &pm)
+{
+    using F = Fmt<DT>;
+    constexpr int EPW = F::EPW;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float acc[EPW];
+        F::unpack(x[0][i], acc);
+#pragma unroll
+        for (int r = 1; r < R; ++r) {
+            float t[EPW];
+            F::unpack(x[r][i], t);
+#pragma unroll
+            for (int e = 0; e < EPW; ++e)
+                acc[e] = acc[e] + t[e];
+        }
+        float av[EPW], rsd[EPW], hf[EPW];
+        F::unpack(F::pack(acc), av);  // a = RNE_T(sum)
+        F::unpack(x[R][i], rsd);
+#pragma unroll
+        for (int e = 0; e < EPW; ++e)
+            acc[e] = av[e] + rsd[e];
+        const uint32_t hw = F::pack(acc);  // h = RNE_T(a + res)
+        hv[i] = hw;
+        F::unpack(hw, hf);
+#pragma unroll
+        for (int e = 0; e < EPW; ++e) {
+            const double hd = (double)hf[e];
+            ssw[i] = __builtin_fma(hd, hd, ssw[i]);  // h^2 is exact in fp64
+        }
+        if constexpr (FP8) {
+            float wf[EPW];
+            F::unpack(w[i], wf);
+#pragma unroll
+            for (int e = 0; e < EPW; ++e) {
+                const double we = (double)wf[e] + gadd;
+                pm = __builtin_fmax(pm, __builtin_fabs((double)hf[e] * we));
+            }
+        }
+    }
+}
+
+// The rows of one block: row group g = blockIdx.x, then g + gridDim.x, ...
+// (with the default grid of one block per row group the loop runs once).
+template <int DT, int R, int PPT, int EPI, int WIN>
+ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, const u32x4 (&wv)[PPT],
+                        double (&red)[2][kMaxWavesPerBlock][2])
 {
     using F = Fmt<DT>;
     constexpr int EPW = F::EPW;
     constexpr bool FP8 = (EPI != EPI_T);
     constexpr bool OUT_T = (EPI != EPI_FP8);
+    constexpr int NS = R + 1;        // input streams
+    constexpr int NL = PPT * NS;     // loads per thread and row
+    constexpr int W = WIN < NL ? WIN : NL;
     // w_eff = w + gadd: 1 under gemma_norm, else -0.0, which adds nothing to
     // any value (signed zeros included), so one fp64 add serves both modes
     const double gadd = a.gemma ? 1.0 : -0.0;
     // plain weights with 16-bit data: the product h * w needs no fp64
     const bool plain_product = DT != DT_FP32 && !a.gemma;
     const bool exact_only = a.exact_only != 0;
-    const long long row = g * c.rpb + c.slot;
-    const bool valid = row < a.M;
     const int rb = c.P * 16;
+    int parity = 0;
 
-    // ---- rank sum, residual add, sum of squares (and max |h * w_eff|)
-    u32x4 hv[PPT];
-    double ssw[4] = {0.0, 0.0, 0.0, 0.0};  // one partial sum of squares per word
-    double pm = 0.0;
-    if (valid) {
-        __amdgpu_buffer_rsrc_t rs[R + 1];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            rs[r] = row_rsrc(a.in[r], row, a.ld_in, rb);
-        rs[R] = row_rsrc(a.residual, row, a.ld_res, rb);
-        const __amdgpu_buffer_rsrc_t rout = row_rsrc(a.residual_out, row, a.ld_rout, rb);
-        constexpr int D = kPrefetch < PPT ? kPrefetch : PPT;
-        u32x4 ring[D + 1][R + 1];
-#pragma unroll
-        for (int k = 0; k < D; ++k)
-            load_pack<R>(rs, (uint32_t)(c.lt + k * c.tpr) * 16u, ring[k % (D + 1)]);
+    for (long long g = blockIdx.x; g < a.groups; g += gridDim.x) {
+        // The weights are loop-invariant; this empty asm hides that from the
+        // compiler, which would otherwise hoist their fp64 conversions out of
+        // the row loop and hold them in registers (several per element).
+        u32x4 w[PPT];
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
-            if (k + D < PPT)
-                load_pack<R>(rs, (uint32_t)(c.lt + (k + D) * c.tpr) * 16u, ring[(k + D) % (D + 1)]);
-            __builtin_amdgcn_sched_barrier(0);
-            const u32x4 (&x)[R + 1] = ring[k % (D + 1)];
+            w[k] = wv[k];
+            asm volatile("" : "+v"(w[k]));
+        }
+        const long long row = g * c.rpb + c.slot;
+        __amdgpu_buffer_rsrc_t sin[NS];
+        in_streams<R>(a, row, rb, sin);
+
+        // ---- rank sum, residual add, sum of squares (and max |h * w_eff|):
+        // load i is stream i % NS of pack i / NS; after issuing load i the
+        // window waits for load i - (W - 1), and a pack is reduced as soon
+        // as its last stream has landed
+        u32x4 x[PPT][NS];
+        u32x4 hv[PPT];
+        double ssw[4] = {0.0, 0.0, 0.0, 0.0};  // one partial sum of squares per word
+        double pm = 0.0;
+        // steps i = 0 .. NL + W - 2, as (kk, r) with i = kk * NS + r
+        constexpr int KK = (NL + W - 1 + NS - 1) / NS;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float acc[EPW];
-                F::unpack(x[0][i], acc);
+        for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-                for (int r = 1; r < R; ++r) {
-                    float t[EPW];
-                    F::unpack(x[r][i], t);
-#pragma unroll
-                    for (int e = 0; e < EPW; ++e)
-                        acc[e] = acc[e] + t[e];
+            for (int r = 0; r < NS; ++r) {
+                const int i = kk * NS + r;
+                if (i >= NL + W - 1)
+                    break;
+                if (i < NL) {
+                    x[kk][r] = bload(sin[r], (uint32_t)(c.lt + kk * c.tpr) * 16u);  // kk < PPT here
+                    wait_vm<W - 1>();
                 }
-                float av[EPW], rsd[EPW], hf[EPW];
-                F::unpack(F::pack(acc), av);  // a = RNE_T(sum)
-                F::unpack(x[R][i], rsd);
-#pragma unroll
-                for (int e = 0; e < EPW; ++e)
-                    acc[e] = av[e] + rsd[e];
-                const uint32_t hw = F::pack(acc);  // h = RNE_T(a + res)
-                hv[k][i] = hw;
-                F::unpack(hw, hf);
-#pragma unroll
-                for (int e = 0; e < EPW; ++e) {
-                    const double hd = (double)hf[e];
-                    ssw[i] = __builtin_fma(hd, hd, ssw[i]);  // h^2 is exact in fp64
+                const int j = i - (W - 1);
+                if (j >= 0 && j % NS == NS - 1) {
+                    const int k = j / NS;
+                    reduce_pack<DT, R, FP8>(x[k], w[k], gadd, hv[k], ssw, pm);
+                    if constexpr (W == NL)
+                        bstore(hv[k], out_stream(a.residual_out, row, a.ld_rout, rb, a.M),
+                               (uint32_t)(c.lt + k * c.tpr) * 16u);
                 }
-                if constexpr (FP8) {
-                    float wf[EPW];
-                    F::unpack(wv[k][i], wf);
+            }
+        }
+        // a throttled row writes residual_out after its loads, so that the
+        // stores never count against the load window
+        if constexpr (W < NL) {
+            const __amdgpu_buffer_rsrc_t rout = out_stream(a.residual_out, row, a.ld_rout, rb, a.M);
+#pragma unroll
+            for (int k = 0; k < PPT; ++k)
+                bstore(hv[k], rout, (uint32_t)(c.lt + k * c.tpr) * 16u);
+        }
+
+        // ---- row reduction: wave DPP tree, then the row group's waves via LDS
+        double ss = (ssw[0] + ssw[1]) + (ssw[2] + ssw[3]);
+        ss = wave_sum_f64(ss);
+        if constexpr (FP8)
+            pm = wave_max_f64(pm);
+        if (c.wpr > 1) {
+            if (c.lane == 0) {
+                red[parity][c.wave][0] = ss;
+                red[parity][c.wave][1] = pm;
+            }
+            lds_barrier();
+            const int w0 = c.slot * c.wpr;
+            ss = red[parity][w0][0];
+            pm = red[parity][w0][1];
+            for (int w = 1; w < c.wpr; ++w) {
+                ss += red[parity][w0 + w][0];
+                if constexpr (FP8)
+                    pm = __builtin_fmax(pm, red[parity][w0 + w][1]);
+            }
+            parity ^= 1;
+        }
+
+        // ---- normalise, write the T output, FP8 epilogue
+        // (h is re-read from its packed T form: keeping phase 1's fp64
+        // conversions alive across the reduction would cost 16 registers a pack)
+        // (the same for the weights: their fp64 forms from phase 1 are not kept)
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            asm volatile("" : "+v"(hv[k]));
+            asm volatile("" : "+v"(w[k]));
+        }
+        const __amdgpu_buffer_rsrc_t rout_t = out_stream(a.out, row, a.ld_out, rb, a.M);
+        const __amdgpu_buffer_rsrc_t rout_q = out_stream(a.fp8_out, row, a.ld_q, rb / 2, a.M);
+        const double rstd = 1.0 / __builtin_sqrt(ss / (double)a.H + (double)a.eps);
+        float scale = 0.0f, inv = 0.0f;
+        bool qfast = false;
+        if constexpr (FP8) {
+            // max |y| = RNE_T(max |h * w_eff| * rstd): rounding is monotone
+            const float amax = round_one<DT>(pm * rstd, exact_only);
+            scale = amax / 448.0f;
+            inv = 1.0f / scale;
+            qfast = !exact_only && scale >= 1.17549435e-38f && scale <= 3.0e38f;
+            if (c.lt == 0 && row < a.M)
+                a.fp8_scale[row] = scale;
+        }
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const uint32_t off = (uint32_t)(c.lt + k * c.tpr) * 16u;
+            u32x4 yv;
+            // lanes with an element on a rounding tie of T, as a wave mask: the
+            // whole wave then recomputes the pack on the exact branch (same
+            // bits for the other lanes), so the branch stays wave-uniform
+            uint64_t risk = exact_only ? ~0ull : 0ull;
+            if (plain_product) {
+                // h * w is exact in fp32 (at most 8 + 8 or 11 + 11 significant bits),
+                // so fl64(h * w) = (double)(h * w): one conversion instead of two
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float hf[EPW], wf[EPW], yf[EPW];
+                    F::unpack(hv[k][i], hf);
+                    F::unpack(w[k][i], wf);
+#pragma unroll
+                    for (int e = 0; e < EPW; ++e) {
+                        yf[e] = (float)((double)(hf[e] * wf[e]) * rstd);
+                        risk |= __builtin_amdgcn_ballot_w64(F::tie_risk(yf[e]));
+                    }
+                    yv[i] = F::pack(yf);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float hf[EPW], wf[EPW], yf[EPW];
+                    F::unpack(hv[k][i], hf);
+                    F::unpack(w[k][i], wf);
 #pragma unroll
                     for (int e = 0; e < EPW; ++e) {
                         const double we = (double)wf[e] + gadd;
-                        pm = __builtin_fmax(pm, __builtin_fabs((double)hf[e] * we));
+                        yf[e] = (float)(((double)hf[e] * we) * rstd);
+                        risk |= __builtin_amdgcn_ballot_w64(F::tie_risk(yf[e]));
                     }
+                    yv[i] = F::pack(yf);
                 }
             }
-            bstore(hv[k], rout, (uint32_t)(c.lt + k * c.tpr) * 16u);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-
-    // ---- row reduction: wave DPP tree, then the row group's waves via LDS
-    double ss = (ssw[0] + ssw[1]) + (ssw[2] + ssw[3]);
-    ss = wave_sum_f64(ss);
-    if constexpr (FP8)
-        pm = wave_max_f64(pm);
-    if (c.wpr > 1) {
-        if (c.lane == 0) {
-            red[parity][c.wave][0] = ss;
-            red[parity][c.wave][1] = pm;
-        }
-        lds_barrier();
-        const int w0 = c.slot * c.wpr;
-        ss = red[parity][w0][0];
-        pm = red[parity][w0][1];
-        for (int w = 1; w < c.wpr; ++w) {
-            ss += red[parity][w0 + w][0];
-            if constexpr (FP8)
-                pm = __builtin_fmax(pm, red[parity][w0 + w][1]);
-        }
-        parity ^= 1;
-    }
-    if (!valid)
-        return;
-
-    // ---- normalise, write the T output, FP8 epilogue
-    const double rstd = 1.0 / __builtin_sqrt(ss / (double)a.H + (double)a.eps);
-    float scale = 0.0f, inv = 0.0f;
-    bool qfast = false;
-    if constexpr (FP8) {
-        // max |y| = RNE_T(max |h * w_eff| * rstd): rounding is monotone
-        const float amax = round_one<DT>(pm * rstd, exact_only);
-        scale = amax / 448.0f;
-        inv = 1.0f / scale;
-        qfast = !exact_only && scale >= 1.17549435e-38f && scale <= 3.0e38f;
-        if (c.lt == 0)
-            a.fp8_scale[row] = scale;
-    }
-    const __amdgpu_buffer_rsrc_t rout_t = row_rsrc(a.out, row, a.ld_out, rb);
-    const __amdgpu_buffer_rsrc_t rout_q = row_rsrc(a.fp8_out, row, a.ld_q, rb / 2);
+            if (risk != 0) {
 #pragma unroll
-    for (int k = 0; k < PPT; ++k) {
-        const uint32_t off = (uint32_t)(c.lt + k * c.tpr) * 16u;
-        u32x4 yv;
-        bool risk = exact_only;
-        if (plain_product) {
-            // h * w is exact in fp32 (at most 8 + 8 or 11 + 11 significant bits),
-            // so fl64(h * w) = (double)(h * w): one conversion instead of two
+                for (int i = 0; i < 4; ++i) {
+                    float hf[EPW], wf[EPW], yf[EPW];
+                    F::unpack(hv[k][i], hf);
+                    F::unpack(w[k][i], wf);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float hf[EPW], wf[EPW], yf[EPW];
-                F::unpack(hv[k][i], hf);
-                F::unpack(wv[k][i], wf);
-#pragma unroll
-                for (int e = 0; e < EPW; ++e) {
-                    yf[e] = (float)((double)(hf[e] * wf[e]) * rstd);
-                    risk |= F::tie_risk(yf[e]);
+                    for (int e = 0; e < EPW; ++e) {
+                        const double we = (double)wf[e] + gadd;
+                        yf[e] = F::exact(((double)hf[e] * we) * rstd);
+                    }
+                    yv[i] = F::pack(yf);
                 }
-                yv[i] = F::pack(yf);
             }
-        } else {
+            if constexpr (OUT_T)
+                bstore(yv, rout_t, off);
+            if constexpr (FP8 && DT != DT_FP32) {
+                float y[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float hf[EPW], wf[EPW], yf[EPW];
-                F::unpack(hv[k][i], hf);
-                F::unpack(wv[k][i], wf);
-#pragma unroll
-                for (int e = 0; e < EPW; ++e) {
-                    const double we = (double)wf[e] + gadd;
-                    yf[e] = (float)(((double)hf[e] * we) * rstd);
-                    risk |= F::tie_risk(yf[e]);
+                for (int i = 0; i < 4; ++i) {
+                    float t[2];
+                    F::unpack(yv[i], t);
+                    y[2 * i] = t[0];
+                    y[2 * i + 1] = t[1];
                 }
-                yv[i] = F::pack(yf);
-            }
-        }
-        if (risk) {
+                u32x2 q = {0u, 0u};
+                uint64_t slow = qfast ? 0ull : ~0ull;  // wave mask, as for risk
+                if (qfast) {
+                    float cq[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float hf[EPW], wf[EPW], yf[EPW];
-                F::unpack(hv[k][i], hf);
-                F::unpack(wv[k][i], wf);
-#pragma unroll
-                for (int e = 0; e < EPW; ++e) {
-                    const double we = (double)wf[e] + gadd;
-                    yf[e] = F::exact(((double)hf[e] * we) * rstd);
+                    for (int e = 0; e < 8; ++e) {
+                        cq[e] = y[e] * inv;
+                        const uint32_t u = __float_as_uint(cq[e]) & 0x7fffffffu;
+                        const uint32_t lo = u & 0xfffffu;
+                        // normal E4M3 range [2^-6, 464) and at least 4 fp32 ulps from
+                        // an E4M3 tie: y * (1/scale) then rounds like y / scale
+                        const bool ok = (u >= 0x3C800000u) & (u < 0x43E80000u) &
+                                        ((lo + 3u - 0x80000u) > 6u);
+                        slow |= __builtin_amdgcn_ballot_w64(!ok);
+                    }
+                    q.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[0], cq[1], 0, false);
+                    q.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[2], cq[3], (int)q.x, true);
+                    q.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[4], cq[5], 0, false);
+                    q.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[6], cq[7], (int)q.y, true);
                 }
-                yv[i] = F::pack(yf);
-            }
-        }
-        if constexpr (OUT_T)
-            bstore(yv, rout_t, off);
-        if constexpr (FP8 && DT != DT_FP32) {
-            float y[8];
+                if (slow != 0) {
+                    uint32_t qb[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float t[2];
-                F::unpack(yv[i], t);
-                y[2 * i] = t[0];
-                y[2 * i + 1] = t[1];
-            }
-            u32x2 q = {0u, 0u};
-            bool slow = !qfast;
-            if (qfast) {
-                float cq[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    cq[e] = y[e] * inv;
-                    const uint32_t u = __float_as_uint(cq[e]) & 0x7fffffffu;
-                    const uint32_t lo = u & 0xfffffu;
-                    // normal E4M3 range [2^-6, 464) and at least 4 fp32 ulps from
-                    // an E4M3 tie: y * (1/scale) then rounds like y / scale
-                    const bool ok = (u >= 0x3C800000u) & (u < 0x43E80000u) &
-                                    ((lo + 3u - 0x80000u) > 6u);
-                    slow |= !ok;
+                    for (int e = 0; e < 8; ++e)
+                        qb[e] = scale == 0.0f ? ((__float_as_uint(y[e]) >> 24) & 0x80u)
+                                              : e4m3_encode(y[e] / scale);
+                    q.x = qb[0] | (qb[1] << 8) | (qb[2] << 16) | (qb[3] << 24);
+                    q.y = qb[4] | (qb[5] << 8) | (qb[6] << 16) | (qb[7] << 24);
                 }
-                q.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[0], cq[1], 0, false);
-                q.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[2], cq[3], (int)q.x, true);
-                q.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[4], cq[5], 0, false);
-                q.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[6], cq[7], (int)q.y, true);
+                bstore8(q, rout_q, off / 2u);
             }
-            if (slow) {
-                uint32_t qb[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    qb[e] = scale == 0.0f ? ((__float_as_uint(y[e]) >> 24) & 0x80u)
-                                          : e4m3_encode(y[e] / scale);
-                q.x = qb[0] | (qb[1] << 8) | (qb[2] << 16) | (qb[3] << 24);
-                q.y = qb[4] | (qb[5] << 8) | (qb[6] << 16) | (qb[7] << 24);
-            }
-            bstore8(q, rout_q, off / 2u);
         }
     }
 }
 
-template <int DT, int R, int PPT, int EPI>
-__global__ void __launch_bounds__(512) row_kernel(const RowArgs a)
+// Blocks of up to 1024 threads for one pack per thread (a whole wide row per
+// block), 512 otherwise (more packs per thread hold more registers).
+template <int DT, int R, int PPT, int EPI, int WIN>
+__global__ void __launch_bounds__(PPT == 1 ? 1024 : 512) row_kernel(const RowArgs a)
 {
     RowCtx c;
     const int tid = threadIdx.x;
     c.tpr = a.tpr;
     c.wpr = c.tpr >> 6;
-    c.rpb = (int)blockDim.x / c.tpr;
+    c.rpb = a.rpb;
     // a wave never straddles two row groups (tpr is a multiple of 64), so the
     // row-group index is wave-uniform: keep it in a scalar register
-    c.slot = __builtin_amdgcn_readfirstlane(tid / c.tpr);
+    c.slot = __builtin_amdgcn_readfirstlane((tid >> 6) / c.wpr);
     c.lt = tid - c.slot * c.tpr;
     c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     c.lane = tid & 63;
@@ -537,6 +617,7 @@ __global__ void __launch_bounds__(512) row_kernel(const RowArgs a)
 
     __shared__ double red[2][kMaxWavesPerBlock][2];
 
+    // the weights: the same columns for every row of the block
     u32x4 wv[PPT];
     {
         const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
@@ -546,12 +627,7 @@ __global__ void __launch_bounds__(512) row_kernel(const RowArgs a)
             wv[k] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (uint32_t)(c.lt + k * c.tpr) * 16u, 0, 0));
     }
-
-    // One row group per block: every row is in flight at once (as far as the
-    // device holds the blocks), and the hardware dispatcher starts a new block
-    // as soon as one retires.
-    int parity = 0;
-    process_rows<DT, R, PPT, EPI>(a, c, (long long)blockIdx.x, wv, red, parity);
+    row_loop<DT, R, PPT, EPI, WIN>(a, c, wv, red);
 }
 
 // --------------------------------------------------------------------------
@@ -624,15 +700,68 @@ __global__ void __launch_bounds__(kFlatThreads) flat_kernel(const FlatArgs a)
 
 // --------------------------------------------------------------------------
 // Launch helpers (instantiated per dtype by kern_*.hip).
+
+// Compute units of the current device (cached per device).
+static int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Blocks of row_kernel<.., kWindowLow> one compute unit holds at this block
+// size (cached per block size; 0 if the runtime cannot tell).
+template <int DT, int R, int PPT, int EPI>
+static int blocks_per_cu(int block)
+{
+    static std::atomic<int> cache[1024 / 64 + 1];
+    const int slot = block / 64;
+    int n = cache[slot].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_kernel<DT, R, PPT, EPI, kWindowLow>, block, 0) !=
+            hipSuccess) {
+            (void)hipGetLastError();
+            return 0;
+        }
+        cache[slot].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <int DT, int R, int PPT, int EPI>
 static hipError_t row_go(const RowArgs &a, const RowShape &s, hipStream_t st)
 {
     const int block = s.tpr * s.rpb;
     const long long groups = (a.M + s.rpb - 1) / s.rpb;
-    if (groups > 0x7fffffffLL)
+    const long long grid = (s.grid > 0 && s.grid < groups) ? s.grid : groups;
+    if (grid > 0x7fffffffLL || block > (PPT == 1 ? 1024 : 512) || s.tpr != a.tpr)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((row_kernel<DT, R, PPT, EPI>), dim3((unsigned)groups), dim3((unsigned)block), 0, st,
-                       a);
+    RowArgs b = a;
+    b.rpb = s.rpb;
+    b.groups = groups;
+    bool low = s.window == 1;
+    if (s.window == 0) {
+        // the narrow window when the whole launch is resident at once and its
+        // input streams exceed 16 MiB (then the window, not the launch size,
+        // sets the bytes in flight)
+        const long long resident = (long long)blocks_per_cu<DT, R, PPT, EPI>(block) * device_cus();
+        const long long input = (long long)(R + 1) * a.M * a.P * 16;
+        low = grid <= resident && input > (16ll << 20);
+    }
+    if (low)
+        hipLaunchKernelGGL((row_kernel<DT, R, PPT, EPI, kWindowLow>), dim3((unsigned)grid), dim3((unsigned)block), 0,
+                           st, b);
+    else
+        hipLaunchKernelGGL((row_kernel<DT, R, PPT, EPI, kWindowHigh>), dim3((unsigned)grid), dim3((unsigned)block),
+                           0, st, b);
     return hipGetLastError();
 }
 

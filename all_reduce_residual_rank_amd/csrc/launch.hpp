@@ -11,7 +11,7 @@ namespace arrms {
 enum Dtype { DT_BF16 = 0, DT_FP16 = 1, DT_FP32 = 2 };
 
 constexpr int kMaxRanks = 8;
-constexpr int kMaxWavesPerBlock = 8;   // row kernel blocks are at most 512 threads
+constexpr int kMaxWavesPerBlock = 16;  // row kernel blocks are at most 1024 threads
 
 // Arguments of the row kernel (one-stage, and stage 2 of two-stage with R = 1
 // and the staging buffer as its only input). Pointers are to 16-byte packs.
@@ -29,6 +29,8 @@ struct RowArgs {
     long long ld_in, ld_res, ld_out, ld_rout, ld_q;
     int H;                // elements per row
     int tpr;              // threads per row group (multiple of 64)
+    int rpb;              // row groups per block (set by the launcher)
+    long long groups;     // row groups in all, ceil(M / rpb) (set by the launcher)
     float eps;
     int gemma;
     int exact_only;
@@ -50,13 +52,17 @@ struct FlatArgs {
 };
 
 // Row kernel shape: PPT packs per thread per row, tpr threads per row,
-// rpb rows per block (one block per group of rpb rows); tail = tpr * PPT >
-// packs per row.
+// rpb rows side by side per block; tail = tpr * PPT > packs per row. grid is
+// the number of blocks: 0 (or at least the number of row groups) gives one
+// block per group of rpb rows; fewer blocks each take every grid-th group in
+// turn. window: phase-1 load window, 0 automatic, 1 narrow, 2 wide.
 struct RowShape {
     int ppt;
     int tpr;
     int rpb;
     bool tail;
+    int grid;
+    int window;
 };
 
 constexpr int kFlatThreads = 256;

@@ -164,17 +164,23 @@ ARRMS_API int arrms_allreduce_sum(const void *const *rank_in, int R, void *out, 
  * arrms_fused_config -- arrms_fused with an explicit launch shape for the row
  * kernel, for benchmarking and tuning (the automatic choice is the shape
  * arrms_fused takes). ppt: 16-byte packs per thread and row (1, 2 or 4); tpr:
- * threads per row (a multiple of 64, at most 512, tpr * ppt covering the row);
+ * threads per row (a multiple of 64, tpr * ppt covering the row);
  * rows_per_block: rows handled side by side by one block (tpr *
- * rows_per_block <= 512). 0 in any of them keeps the automatic value; a
- * negative value gives ARRMS_ERR_INVALID and a shape that cannot cover a row
- * ARRMS_ERR_UNSUPPORTED. All other arguments, the results and the error
- * behaviour are arrms_fused's.
+ * rows_per_block at most 1024 threads with ppt = 1, else 512); blocks: the
+ * number of blocks launched -- with fewer blocks than row groups each block
+ * takes every blocks-th group of rows in turn; load_window: how many 16-byte
+ * loads a thread keeps in flight -- 1 a narrow window (for large launches
+ * whose rows are all resident at once), 2 a wide one (the whole row, up to a
+ * cap). 0 in any of them keeps the automatic value; a negative value (or a
+ * load_window above 2) gives ARRMS_ERR_INVALID and a shape that cannot cover
+ * a row ARRMS_ERR_UNSUPPORTED. All other arguments, the results and the
+ * error behaviour are arrms_fused's.
  */
 ARRMS_API int arrms_fused_config(const void *const *rank_in, int R, const void *residual,
                                  const void *weight, void *out, void *residual_out, void *fp8_out,
                                  float *fp8_scale, int M, int H, float eps, int flags, int ppt,
-                                 int tpr, int rows_per_block, hipStream_t stream);
+                                 int tpr, int rows_per_block, int blocks, int load_window,
+                                 hipStream_t stream);
 
 /*
  * arrms_reserve_staging -- allocate the staging buffer of the two-stage path

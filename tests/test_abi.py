@@ -198,3 +198,16 @@ def test_allreduce_sum_argument_checks():
     for kw in (dict(n=4100), dict(n=2050, flags=arrms.DTYPE_FP32), dict(out=BASE + 12 * STRIDE + 8),
                dict(in3=BASE + 3 * STRIDE + 4)):
         assert _sum(**kw) == arrms.ERR_UNSUPPORTED, kw
+
+
+def test_fused_config_argument_checks():
+    ptr = [BASE + r * STRIDE for r in range(4)]
+    args = (ptr, 4, BASE + 10 * STRIDE, BASE + 11 * STRIDE, BASE + 12 * STRIDE, BASE + 13 * STRIDE,
+            None, None, 0, 64, 1e-6, 0)
+    assert arrms.arrms_fused_config_raw(*args, 0, 0, 0, 0, None) == arrms.OK
+    assert arrms.arrms_fused_config_raw(*args, 0, 0, 0, 0, None, load_window=2) == arrms.OK
+    for bad in ((-1, 0, 0, 0, 0), (0, -64, 0, 0, 0), (0, 0, -1, 0, 0), (0, 0, 0, -5, 0), (0, 0, 0, 0, 3),
+                (0, 0, 0, 0, -1)):
+        ppt, tpr, rpb, blocks, win = bad
+        assert arrms.arrms_fused_config_raw(*args, ppt, tpr, rpb, blocks, None, load_window=win) == \
+            arrms.ERR_INVALID, bad

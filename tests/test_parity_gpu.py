@@ -270,3 +270,53 @@ def test_small_staging_forces_many_chunks():
     finally:
         torch.cuda.synchronize()
         arrms.arrms_release_staging()
+
+
+def _run_config(wl, xs, res, w, flags, ppt, tpr, rpb, blocks, window):
+    dev = torch.device("cuda")
+    T = gu.TORCH_T[wl.dtype]
+    M, H = res.shape
+    fp8 = bool(flags & arrms.FP8)
+    xd = [x.to(dev) for x in xs]
+    rd, wd = res.to(dev), w.to(dev)
+    out = gu.poison_(torch.empty(M, H, dtype=T, device=dev)) if (wl.mirror or not fp8) else None
+    rout = gu.poison_(torch.empty(M, H, dtype=T, device=dev))
+    q = gu.poison_(torch.empty(M, H, dtype=torch.uint8, device=dev)) if fp8 else None
+    sc = gu.poison_(torch.empty(M, dtype=torch.float32, device=dev)) if fp8 else None
+    arrms.arrms_fused_config(xd, rd, wd, out, rout, q, sc, eps=wl.eps, flags=flags, ppt=ppt, tpr=tpr,
+                             rows_per_block=rpb, blocks=blocks, load_window=window, M=M, H=H)
+    torch.cuda.synchronize()
+    return {"out": None if out is None else gu.host_bits(out), "residual_out": gu.host_bits(rout),
+            "fp8": None if q is None else gu.host_bits(q), "scale": None if sc is None else gu.host_bits(sc)}
+
+
+# (ppt, tpr, rows_per_block, blocks, load_window): one row group per block,
+# row loops over a few blocks (every block takes several rows in turn),
+# several row groups side by side per block, wide one-pack blocks, and both
+# phase-1 load windows
+SHAPES = [(0, 0, 0, 0, 0), (0, 0, 0, 7, 0), (0, 0, 0, 64, 1), (1, 0, 0, 5, 2), (2, 0, 0, 33, 1),
+          (4, 0, 0, 3, 2), (2, 0, 2, 11, 2), (1, 0, 0, 1, 1), (4, 0, 0, 0, 1), (4, 0, 0, 0, 2),
+          (2, 0, 0, 0, 1), (1, 0, 0, 0, 2)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "ppt%d-tpr%d-rpb%d-b%d-w%d" % s)
+@pytest.mark.parametrize("wl", [
+    wlmod.Workload("cfg_bf16", R=4, M=131, H=6144, row_scale=(0.1, 10.0)),
+    wlmod.Workload("cfg_fp16_fp8", R=3, M=77, H=2880, dtype="fp16", gemma=True, fp8=True, mirror=True,
+                   w_mean=0.0),
+    wlmod.Workload("cfg_r8_7168", R=8, M=45, H=7168, eps=1e-5),
+    wlmod.Workload("cfg_fp32", R=2, M=60, H=512, dtype="fp32"),
+], ids=lambda w: w.name)
+def test_launch_shapes_match_oracle(wl, shape):
+    ppt, tpr, rpb, blocks, window = shape
+    P = wl.H * wl.esize // 16
+    if ppt:
+        need = -(-P // ppt)
+        need = -(-need // 64) * 64
+        if need * max(rpb, 1) > (1024 if ppt == 1 else 512):
+            pytest.skip("shape cannot cover this row")
+    xs, res, w = wlmod.make_inputs(wl, seed=12)
+    want = gu.run_oracle(wl, xs, res, w)
+    print(f"case {wl.name} shape={shape}", flush=True)
+    got = _run_config(wl, xs, res, w, wl.flags | PATHS["one"], ppt, tpr, rpb, blocks, window)
+    gu.compare(got, want, wl.dtype, label=f"{wl.name}/{shape}")
