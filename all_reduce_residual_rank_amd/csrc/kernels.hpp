@@ -282,6 +282,12 @@ ARRMS_DEV u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off)
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kBufAuxNT));
 }
 
+// Reused data (the weights): default cache policy.
+ARRMS_DEV u32x4 bload_cached(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 ARRMS_DEV void bstore(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kBufAuxNT);
@@ -301,6 +307,12 @@ ARRMS_DEV void bstore8(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
 // pipeline). Launches that run in several rounds of blocks, or that are
 // small, do better with the wide window (the whole row, up to kWindowHigh
 // loads), which hides each block's latency.
+#ifndef ARRMS_ROUT_LATE_ALL
+#define ARRMS_ROUT_LATE_ALL 0
+#endif
+#ifndef ARRMS_LATE_WEIGHTS
+#define ARRMS_LATE_WEIGHTS 1
+#endif
 constexpr int kWindowLow = 3;
 constexpr int kWindowHigh = 16;
 
@@ -381,8 +393,7 @@ ARRMS_DEV void reduce_pack(const u32x4 (&x)[R + 1], const u32x4 &w, double gadd,
 // The rows of one block: row group g = blockIdx.x, then g + gridDim.x, ...
 // (with the default grid of one block per row group the loop runs once).
 template <int DT, int R, int PPT, int EPI, int WIN>
-ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, const u32x4 (&wv)[PPT],
-                        double (&red)[2][kMaxWavesPerBlock][2])
+ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMaxWavesPerBlock][2])
 {
     using F = Fmt<DT>;
     constexpr int EPW = F::EPW;
@@ -401,14 +412,16 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, const u32x4 (&wv)[PPT
     int parity = 0;
 
     for (long long g = blockIdx.x; g < a.groups; g += gridDim.x) {
-        // The weights are loop-invariant; this empty asm hides that from the
-        // compiler, which would otherwise hoist their fp64 conversions out of
-        // the row loop and hold them in registers (several per element).
+        // The weights (the same columns for every row, from L2) are read per
+        // row: with FP8 before the row's inputs (the row maximum needs them in
+        // phase 1), otherwise once the inputs are all issued, so that they
+        // neither hold registers through phase 1 nor sit in the load window.
+        const __amdgpu_buffer_rsrc_t rw = row_rsrc(a.weight, 0, 0, rb);
         u32x4 w[PPT];
+        if constexpr (FP8 || !ARRMS_LATE_WEIGHTS) {
 #pragma unroll
-        for (int k = 0; k < PPT; ++k) {
-            w[k] = wv[k];
-            asm volatile("" : "+v"(w[k]));
+            for (int k = 0; k < PPT; ++k)
+                w[k] = bload_cached(rw, (uint32_t)(c.lt + k * c.tpr) * 16u);
         }
         const long long row = g * c.rpb + c.slot;
         __amdgpu_buffer_rsrc_t sin[NS];
@@ -435,23 +448,22 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, const u32x4 (&wv)[PPT
                     x[kk][r] = bload(sin[r], (uint32_t)(c.lt + kk * c.tpr) * 16u);  // kk < PPT here
                     wait_vm<W - 1>();
                 }
+                if constexpr (!FP8 && ARRMS_LATE_WEIGHTS) {
+                    if (i == NL - 1) {
+#pragma unroll
+                        for (int k = 0; k < PPT; ++k)
+                            w[k] = bload_cached(rw, (uint32_t)(c.lt + k * c.tpr) * 16u);
+                    }
+                }
                 const int j = i - (W - 1);
                 if (j >= 0 && j % NS == NS - 1) {
                     const int k = j / NS;
                     reduce_pack<DT, R, FP8>(x[k], w[k], gadd, hv[k], ssw, pm);
-                    if constexpr (W == NL)
+                    if constexpr (W == NL && !ARRMS_ROUT_LATE_ALL)
                         bstore(hv[k], out_stream(a.residual_out, row, a.ld_rout, rb, a.M),
                                (uint32_t)(c.lt + k * c.tpr) * 16u);
                 }
             }
-        }
-        // a throttled row writes residual_out after its loads, so that the
-        // stores never count against the load window
-        if constexpr (W < NL) {
-            const __amdgpu_buffer_rsrc_t rout = out_stream(a.residual_out, row, a.ld_rout, rb, a.M);
-#pragma unroll
-            for (int k = 0; k < PPT; ++k)
-                bstore(hv[k], rout, (uint32_t)(c.lt + k * c.tpr) * 16u);
         }
 
         // ---- row reduction: wave DPP tree, then the row group's waves via LDS
@@ -487,6 +499,15 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, const u32x4 (&wv)[PPT
         }
         const __amdgpu_buffer_rsrc_t rout_t = out_stream(a.out, row, a.ld_out, rb, a.M);
         const __amdgpu_buffer_rsrc_t rout_q = out_stream(a.fp8_out, row, a.ld_q, rb / 2, a.M);
+        // a throttled row writes residual_out once the row is reduced: the
+        // stores never count against the load window, and the row's reads
+        // are over before its writes begin (measured faster on MI355X)
+        if constexpr (W < NL || ARRMS_ROUT_LATE_ALL) {
+            const __amdgpu_buffer_rsrc_t rout = out_stream(a.residual_out, row, a.ld_rout, rb, a.M);
+#pragma unroll
+            for (int k = 0; k < PPT; ++k)
+                bstore(hv[k], rout, (uint32_t)(c.lt + k * c.tpr) * 16u);
+        }
         const double rstd = 1.0 / __builtin_sqrt(ss / (double)a.H + (double)a.eps);
         float scale = 0.0f, inv = 0.0f;
         bool qfast = false;
@@ -617,17 +638,7 @@ __global__ void __launch_bounds__(PPT == 1 ? 1024 : 512) row_kernel(const RowArg
 
     __shared__ double red[2][kMaxWavesPerBlock][2];
 
-    // the weights: the same columns for every row of the block
-    u32x4 wv[PPT];
-    {
-        const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)a.weight, (short)0, c.P * 16, kBufDword3);
-#pragma unroll
-        for (int k = 0; k < PPT; ++k)
-            wv[k] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (uint32_t)(c.lt + k * c.tpr) * 16u, 0, 0));
-    }
-    row_loop<DT, R, PPT, EPI, WIN>(a, c, wv, red);
+    row_loop<DT, R, PPT, EPI, WIN>(a, c, red);
 }
 
 // --------------------------------------------------------------------------
@@ -646,37 +657,54 @@ ARRMS_DEV void flat_packs(const FlatArgs &a, long long src_row, long long dst_ro
 {
     using F = Fmt<DT>;
     constexpr int EPW = F::EPW;
-    u32x4 xv[R][kFlatPacksPerThread];
+    constexpr int NP = kFlatPacksPerThread;
+    constexpr int NL = NP * R;
+    constexpr int W = kFlatWindow < NL ? kFlatWindow : NL;
+    u32x4 xv[NP][R];
+    u32x4 out[NP];
+    // loads in a sliding window (pack-major, ranks in order); a pack is
+    // reduced as soon as its last rank has landed; the stores follow the loads
+    constexpr int KK = (NL + W - 1 + R - 1) / R;
 #pragma unroll
-    for (int k = 0; k < kFlatPacksPerThread; ++k)
-        if (ok[k]) {
+    for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-            for (int r = 0; r < R; ++r)
-                xv[r][k] = ld16_nt(a.in[r], src_row + j[k]);
+        for (int r = 0; r < R; ++r) {
+            const int i = kk * R + r;
+            if (i >= NL + W - 1)
+                break;
+            if (i < NL) {
+                if (ok[kk])
+                    xv[kk][r] = ld16_nt(a.in[r], src_row + j[kk]);  // kk < NP here
+                wait_vm<W - 1>();
+            }
+            const int jj = i - (W - 1);
+            if (jj >= 0 && jj % R == R - 1) {
+                const int k = jj / R;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float acc[EPW];
+                    F::unpack(xv[k][0][q], acc);
+#pragma unroll
+                    for (int rr = 1; rr < R; ++rr) {
+                        float t[EPW];
+                        F::unpack(xv[k][rr][q], t);
+#pragma unroll
+                        for (int e = 0; e < EPW; ++e)
+                            acc[e] = acc[e] + t[e];
+                    }
+                    out[k][q] = F::pack(acc);
+                }
+            }
         }
+    }
 #pragma unroll
-    for (int k = 0; k < kFlatPacksPerThread; ++k) {
+    for (int k = 0; k < NP; ++k) {
         if (!ok[k])
             continue;
-        u32x4 out;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float acc[EPW];
-            F::unpack(xv[0][k][i], acc);
-#pragma unroll
-            for (int r = 1; r < R; ++r) {
-                float t[EPW];
-                F::unpack(xv[r][k][i], t);
-#pragma unroll
-                for (int e = 0; e < EPW; ++e)
-                    acc[e] = acc[e] + t[e];
-            }
-            out[i] = F::pack(acc);
-        }
         if constexpr (NTS)
-            st16_nt(a.dst, dst_row + j[k], out);
+            st16_nt(a.dst, dst_row + j[k], out[k]);
         else
-            st16(a.dst, dst_row + j[k], out);
+            st16(a.dst, dst_row + j[k], out[k]);
     }
 }
 
