@@ -175,24 +175,26 @@ int choose_path(int M, int H, int R, int flags)
     return ARRMS_PATH_ONE_STAGE;
 }
 
-// Row-kernel shape for P packs per row: PPT in {1,2,4}, tpr = the PPT-covering
-// multiple of 64 up to 512. Prefer an exact cover (no idle lanes), then the
+// Row kernel launch shape: packs per thread (PPT) in 1..4, threads per row
+// tpr = the PPT-covering multiple of 64, at most 512. Exact cover first, then
 // least padding, then more packs per thread (fewer, busier threads: measured
-// faster on MI355X) as long as a thread's R+1 input packs stay within 20
-// (80 registers), which keeps several blocks resident per compute unit. The
-// FP8 epilogue has more per-element work after the row reduction; spreading
-// it over more threads (at most 2 packs each) measured faster.
+// faster on MI355X for large launches) as long as a thread's R+1 input packs
+// stay within 20 (80 registers). Launches of fewer than 512 rows cap PPT at 2
+// (more threads per row make up for the few rows), and the FP8 epilogue, with
+// more per-element work after the row reduction, caps it at 3.
 arrms::RowShape choose_shape(int P, int R, long long M, bool fp8)
 {
-    (void)M;
     arrms::RowShape best = {0, 0, 0, false, 0, 0};
     long long best_key = -1;
-    const int ppts[3] = {1, 2, 4};
-    for (int c = 0; c < 3; ++c) {
+    int cap = fp8 ? 3 : 4;
+    if (M < 512 && cap > 2)
+        cap = 2;
+    const int ppts[4] = {1, 2, 3, 4};
+    for (int c = 0; c < 4; ++c) {
         const int ppt = ppts[c];
-        if (ppt > 1 && ppt * (R + 1) > 20)
+        if (ppt > cap)
             continue;
-        if (fp8 && ppt > 2)
+        if (ppt > 1 && ppt * (R + 1) > 20)
             continue;
         int tpr = (P + ppt - 1) / ppt;
         tpr = (tpr + 63) / 64 * 64;
@@ -207,7 +209,7 @@ arrms::RowShape choose_shape(int P, int R, long long M, bool fp8)
     }
     if (best.ppt == 0) {
         // wide rows with many ranks: the register budget gives way to coverage
-        for (int c = 0; c < 3 && best.ppt == 0; ++c) {
+        for (int c = 0; c < 4 && best.ppt == 0; ++c) {
             int tpr = (P + ppts[c] - 1) / ppts[c];
             tpr = (tpr + 63) / 64 * 64;
             if (tpr <= 512)
@@ -367,7 +369,7 @@ bool apply_shape(const ShapeReq *req, int P, int R, long long M, arrms::RowShape
     if (!req)
         return true;
     if (req->ppt) {
-        if (req->ppt != 1 && req->ppt != 2 && req->ppt != 4)
+        if (req->ppt < 1 || req->ppt > 4)
             return false;
         s.ppt = req->ppt;
         int tpr = (P + s.ppt - 1) / s.ppt;
@@ -502,9 +504,9 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
             b.fp8_scale = fp8_scale + m0;
         }
         b.M = n;
-        // the row pass takes the one-stage shape of these rows, so both paths
+        // the row pass takes the one-stage shape of the whole launch, so both paths
         // reduce the row statistics in the same order and give the same bits
-        arrms::RowShape s = choose_shape(P, R, n, fp8);
+        arrms::RowShape s = choose_shape(P, R, M, fp8);
         if (s.ppt == 0 || !apply_shape(req, P, R, n, s))
             return ARRMS_ERR_UNSUPPORTED;
         b.tpr = s.tpr;

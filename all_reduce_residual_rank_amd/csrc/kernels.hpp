@@ -799,6 +799,7 @@ static hipError_t row_go_r(const RowArgs &a, const RowShape &s, hipStream_t st)
     switch (s.ppt) {
     case 1: return row_go<DT, R, 1, EPI>(a, s, st);
     case 2: return row_go<DT, R, 2, EPI>(a, s, st);
+    case 3: return row_go<DT, R, 3, EPI>(a, s, st);
     case 4: return row_go<DT, R, 4, EPI>(a, s, st);
     default: return hipErrorInvalidValue;
     }
