@@ -92,8 +92,7 @@ template <> struct Fmt<DT_FP16> {
     // or anything below 2^-14 (fp16 subnormals drop more bits): exact branch
     ARRMS_DEV bool tie_risk(float f)
     {
-        uint32_t u = __float_as_uint(f) & 0x7fffffffu;
-        return ((u & 0x1fffu) == 0x1000u) | (u < (113u << 23));
+        return ((__float_as_uint(f) << 19) == 0x80000000u) | (__builtin_fabsf(f) < 0x1p-14f);
     }
     ARRMS_DEV float exact(double v) { return f64_to_f32_odd(v); }
 };
@@ -584,26 +583,43 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
                     y[2 * i + 1] = t[1];
                 }
                 u32x2 q = {0u, 0u};
-                uint64_t slow = qfast ? 0ull : ~0ull;  // wave mask, as for risk
                 if (qfast) {
                     float cq[8];
+                    bool bad[8];
+                    uint64_t anybad = 0;  // wave mask, as for risk
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         cq[e] = y[e] * inv;
-                        const uint32_t u = __float_as_uint(cq[e]) & 0x7fffffffu;
-                        const uint32_t lo = u & 0xfffffu;
-                        // normal E4M3 range [2^-6, 464) and at least 4 fp32 ulps from
-                        // an E4M3 tie: y * (1/scale) then rounds like y / scale
-                        const bool ok = (u >= 0x3C800000u) & (u < 0x43E80000u) &
-                                        ((lo + 3u - 0x80000u) > 6u);
-                        slow |= __builtin_amdgcn_ballot_w64(!ok);
+                        // y * (1/scale) rounds like y / scale when it lies in the normal
+                        // E4M3 range [2^-6, 464) and at least 4 fp32 ulps from an E4M3
+                        // tie: the 20 bits below E4M3's mantissa, moved to the top of a
+                        // word and offset, land at or below 6 << 12 exactly when they are
+                        // within 3 ulps of the halfway pattern 0x80000
+                        const float m = __builtin_fabsf(cq[e]);
+                        const uint32_t t = (__float_as_uint(cq[e]) << 12) + 0x80003000u;
+                        bad[e] = !(m >= 0x1p-6f) | !(m < 464.0f) | (t <= 0x6000u);
+                        anybad |= __builtin_amdgcn_ballot_w64(bad[e]);
                     }
                     q.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[0], cq[1], 0, false);
                     q.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[2], cq[3], (int)q.x, true);
                     q.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[4], cq[5], 0, false);
                     q.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[6], cq[7], (int)q.y, true);
-                }
-                if (slow != 0) {
+                    if (anybad != 0) {
+                        // rare: recompute just those elements, by division and the
+                        // exact encoder
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            if (__builtin_amdgcn_ballot_w64(bad[e]) != 0 && bad[e]) {
+                                const uint32_t b = e4m3_encode(y[e] / scale);
+                                const int sh = 8 * (e & 3);
+                                if (e < 4)
+                                    q.x = (q.x & ~(0xffu << sh)) | (b << sh);
+                                else
+                                    q.y = (q.y & ~(0xffu << sh)) | (b << sh);
+                            }
+                        }
+                    }
+                } else {
                     uint32_t qb[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
