@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--no-hot", action="store_true", help="skip the cache-resident context number")
     p.add_argument("--no-sum", action="store_true",
                    help="skip the plain rank all-reduce (no norm) timing")
+    p.add_argument("--no-strided", action="store_true", help="skip the padded-rows timing")
+    p.add_argument("--replays", type=int, default=20,
+                   help="further timed replays of the chosen path, for median/min (0: none)")
     p.add_argument("--sum-only", action="store_true",
                    help="time only the plain rank all-reduce (R=4, 1024 x 6144 bf16 message)")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -107,23 +110,35 @@ def call(arrms, wl, d, flags, stream):
                       flags=flags, M=wl.M, H=wl.H, stream=stream)
 
 
-def time_graph(torch, calls, steps, warmup):
+def time_graph(torch, calls, steps, warmup, extra=None):
     """Warm up, then time exactly `steps` calls replayed from one HIP graph.
-    calls: functions f(stream) that each enqueue one call; used in turn."""
+    calls: functions f(stream) that each enqueue one call; used in turn.
+    extra: a list that receives the ms of further timed replays (len(extra)
+    given as a count in extra[0]), for the spread; the first timing is the
+    one returned."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     n = len(calls)
-    gw = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gw, stream=s):
-        for i in range(warmup):
-            calls[i % n](s)
     gk = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gk, stream=s):
         for i in range(steps):
             calls[i % n](s)
     torch.cuda.synchronize()
-    with torch.cuda.stream(s):
-        gw.replay()
+    if warmup > 0 and warmup % steps == 0:
+        # warm up with the timed graph itself (its first replays also carry the
+        # graph's one-time upload)
+        with torch.cuda.stream(s):
+            for _ in range(warmup // steps):
+                gk.replay()
+    elif warmup > 0:
+        gw = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gw, stream=s):
+            for i in range(warmup):
+                calls[i % n](s)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            gw.replay()
+        del gw
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -133,13 +148,52 @@ def time_graph(torch, calls, steps, warmup):
         e1.record(s)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
-    del gw, gk
+    if extra:
+        n = int(extra.pop())
+        for _ in range(n):
+            with torch.cuda.stream(s):
+                e0.record(s)
+                gk.replay()
+                e1.record(s)
+            torch.cuda.synchronize()
+            extra.append(e0.elapsed_time(e1))
+    del gk
     return ms
 
 
-def time_path(torch, arrms, wl, sets, flags, steps, warmup):
+def time_path(torch, arrms, wl, sets, flags, steps, warmup, extra=None):
     calls = [lambda st, d=d: call(arrms, wl, d, flags, st) for d in sets.sets]
-    return time_graph(torch, calls, steps, warmup)
+    return time_graph(torch, calls, steps, warmup, extra)
+
+
+def time_strided(torch, arrms, wl, pad, steps, warmup):
+    """The workload through arrms_fused_strided: every matrix a column window
+    of an [M][H + pad] allocation (row stride H + pad elements)."""
+    from all_reduce_residual_rank_amd import workloads as wlmod
+    dev = torch.device("cuda")
+    T = wlmod.DTYPES[wl.dtype]
+    xs, res, w = wlmod.make_inputs(wl, seed=0)
+    ld = wl.H + pad
+
+    def win(src=None):
+        base = torch.empty(wl.M, ld, dtype=T, device=dev)
+        v = base[:, :wl.H]
+        if src is not None:
+            v.copy_(src)
+        return v
+
+    nsets = max(2, -(-ROTATE_BYTES // ((wl.R + 3) * wl.M * ld * wl.esize)))
+    sets = [{"xs": [win(x) for x in xs], "res": win(res), "w": w.to(dev), "out": win(), "rout": win()}
+            for _ in range(nsets)]
+
+    def one(d, st):
+        arrms.arrms_fused_strided(d["xs"], d["res"], d["w"], d["out"], d["rout"], eps=wl.eps,
+                                  flags=wl.flags | arrms.FORCE_ONE_STAGE, stream=st)
+
+    calls = [lambda st, d=d: one(d, st) for d in sets]
+    ms = time_graph(torch, calls, steps, warmup)
+    del sets
+    return ms * 1000.0 / steps
 
 
 def time_sum(torch, arrms, case, R, steps, warmup):
@@ -180,6 +234,29 @@ def time_hot(torch, arrms, wl, sets, flags, reps=64):
     return min(res)
 
 
+def read_clocks():
+    """Current shader and memory clocks from a read-only rocm-smi query, if it
+    answers within a few seconds; else None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=10)
+        d = json.loads(r.stdout)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    card = next((v for k, v in d.items() if k.startswith("card")), None)
+    if not isinstance(card, dict):
+        return None
+    out = {}
+    for key, val in card.items():
+        k = key.lower()
+        if "sclk" in k and "mhz" in str(val).lower():
+            out["sclk"] = val
+        elif "mclk" in k and "mhz" in str(val).lower():
+            out["mclk"] = val
+    return out or None
+
+
 def cpu_baseline(wl, budget_s):
     """The oracle as it stands, single-threaded, on row samples of the workload."""
     import numpy as np
@@ -211,10 +288,29 @@ def cpu_baseline(wl, budget_s):
     t = statistics.median(times)
     e = wl.esize
     metric_bytes = (wl.R + 2) * rows * wl.H * e + wl.H * e
-    return {"value": round(metric_bytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"rows 0..{rows - 1} of the workload ({rows}x{wl.H}, R={wl.R}), "
-                      f"median of {len(times)} runs, {t * 1e3:.1f} ms each",
-            "us_per_row": round(t / rows * 1e6, 3)}
+    out = {"value": round(metric_bytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"rows 0..{rows - 1} of the workload ({rows}x{wl.H}, R={wl.R}), "
+                     f"median of {len(times)} runs, {t * 1e3:.1f} ms each",
+           "us_per_row": round(t / rows * 1e6, 3)}
+    # the same sample split by rows over the host's cores (the oracle's C code
+    # runs outside the GIL), for context
+    from concurrent.futures import ThreadPoolExecutor
+    n = max(1, min(len(os.sched_getaffinity(0)), 16, rows))
+    bounds = [(rows * i // n, rows * (i + 1) // n) for i in range(n)]
+
+    def part(b):
+        oracle.fused(xb, rb, wb, wl.eps, wl.flags & 0xF, rows=b)
+
+    with ThreadPoolExecutor(n) as ex:
+        tt = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            list(ex.map(part, bounds))
+            tt.append(time.perf_counter() - t0)
+    tm = statistics.median(tt)
+    out["threads"] = {"value": round(metric_bytes / tm / 1e9, 4), "cores": n,
+                      "sample": f"the same rows split over {n} threads, median of 3 runs, {tm * 1e3:.1f} ms each"}
+    return out
 
 
 def main():
@@ -264,8 +360,10 @@ def main():
     auto_path = {arrms.PATH_ONE_STAGE: "one", arrms.PATH_TWO_STAGE: "two"}[
         arrms.arrms_query_path(wl.M, wl.H, wl.R, wl.flags)]
     chosen = auto_path if args.path == "auto" else args.path
-    ms = time_path(torch, arrms, wl, sets, wl.flags | path_flags[chosen], args.steps, args.warmup)
+    reps = [float(args.replays)]
+    ms = time_path(torch, arrms, wl, sets, wl.flags | path_flags[chosen], args.steps, args.warmup, reps)
     us = ms * 1000.0 / args.steps
+    rep_us = sorted(r * 1000.0 / args.steps for r in reps)
     metric_bytes = (wl.R + 2) * wl.M * wl.H * e + wl.H * e
     algo_bytes = (wl.R + 3) * wl.M * wl.H * e + wl.H * e
     if wl.fp8:
@@ -296,6 +394,8 @@ def main():
         "us_per_call": round(us, 3), "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
         "metric_bytes": metric_bytes,
         "path_us": other, "hot_us_cache_resident": None if hot is None else round(hot, 3),
+        "replays": None if not rep_us else {"n": len(rep_us), "median_us": round(statistics.median(rep_us), 3),
+                                             "min_us": round(rep_us[0], 3), "max_us": round(rep_us[-1], 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": algo_bytes,
@@ -313,6 +413,16 @@ def main():
                                  "unit": "GB/s", "algorithmic_bytes": sum_bytes,
                                  "frac": round(sum_bytes / (sum_us * 1e-6) / 1e9 / PEAK_GBS, 4),
                                  "kernel": "flat_kernel"}
+    if not args.no_strided and not wl.fp8:
+        # padded rows (row stride H + 64 elements) through arrms_fused_strided
+        st_us = time_strided(torch, arrms, wl, 64, args.steps, args.warmup)
+        line["strided"] = {"row_stride": wl.H + 64, "us_per_call": round(st_us, 3),
+                           "achieved": round(algo_bytes / (st_us * 1e-6) / 1e9, 2), "unit": "GB/s",
+                           "frac": round(algo_bytes / (st_us * 1e-6) / 1e9 / PEAK_GBS, 4),
+                           "kernel": "row_kernel"}
+    clocks = read_clocks()
+    if clocks:
+        line["clocks"] = clocks
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)
