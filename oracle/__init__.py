@@ -25,10 +25,16 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-# flag bits as the oracle reads them (dtype in bits 0-1, gemma_norm, FP8)
+# flag bits as the oracle reads them (dtype in bits 0-1, gemma_norm, and at
+# most one quantised output: per-token FP8, per-group FP8, MXFP4)
 BF16, FP16, FP32 = 0, 1, 2
 GEMMA = 4
 FP8 = 8
+FP8_GROUP = 16
+MXFP4 = 32
+GROUP = 128       # per-group FP8: columns per scale
+MX_BLOCK = 32     # MXFP4: columns per E8M0 scale
+QUANT = FP8 | FP8_GROUP | MXFP4
 
 _lib = None
 
@@ -59,7 +65,8 @@ def _load():
     lib.oracle_rank_sum.argtypes = [ctypes.POINTER(vp), i, vp, ctypes.c_size_t, i]
     lib.oracle_rank_sum.restype = i
     sz = ctypes.c_size_t
-    for name in ("orc_bf16_from_double_n", "orc_fp16_from_double_n", "orc_e4m3_from_float_n"):
+    for name in ("orc_bf16_from_double_n", "orc_fp16_from_double_n", "orc_e4m3_from_float_n",
+                 "orc_e2m1_from_float_n"):
         getattr(lib, name).argtypes = [vp, vp, sz]
         getattr(lib, name).restype = None
     _lib = lib
@@ -79,7 +86,10 @@ def fused(xs, residual, weight, eps: float, flags: int, *, want_out: bool = True
     """Run the oracle on host arrays.
 
     xs: list of R arrays [M][H] (storage bits of T); residual [M][H]; weight [H].
-    flags: dtype | GEMMA | FP8. With FP8, ``want_out`` controls the T mirror.
+    flags: dtype | GEMMA | at most one of FP8, FP8_GROUP, MXFP4. With a
+    quantised output, ``want_out`` controls the T mirror. 'fp8' holds the
+    codes ([M][H] E4M3, or [M][H/2] packed E2M1 for MXFP4) and 'scale' the
+    scales ([M] or [M][H/128] fp32, or [M][H/32] E8M0 bytes).
     rows: optional (begin, end) row range; rows outside it are left zero.
     residual_out_inplace: write residual_out into ``residual`` itself.
     Returns a dict with 'out', 'residual_out', 'fp8', 'scale' (absent ones None).
@@ -97,11 +107,16 @@ def fused(xs, residual, weight, eps: float, flags: int, *, want_out: bool = True
         residual = np.ascontiguousarray(residual, dtype=sdt)
     weight = np.ascontiguousarray(weight, dtype=sdt).reshape(H)
     b, e = rows if rows is not None else (0, M)
-    fp8 = bool(flags & FP8)
+    quant = flags & QUANT
     out = np.zeros((M, H), dtype=sdt) if want_out else None
     res_out = residual if residual_out_inplace else np.zeros((M, H), dtype=sdt)
-    q = np.zeros((M, H), dtype=np.uint8) if fp8 else None
-    sc = np.zeros((M,), dtype=np.float32) if fp8 else None
+    q = sc = None
+    if quant == FP8:
+        q, sc = np.zeros((M, H), dtype=np.uint8), np.zeros((M,), dtype=np.float32)
+    elif quant == FP8_GROUP:
+        q, sc = np.zeros((M, H), dtype=np.uint8), np.zeros((M, H // GROUP), dtype=np.float32)
+    elif quant == MXFP4:
+        q, sc = np.zeros((M, H // 2), dtype=np.uint8), np.zeros((M, H // MX_BLOCK), dtype=np.uint8)
     ptrs = (ctypes.c_void_p * len(xs))(*[x.ctypes.data for x in xs])
     scratch = np.empty((H,), dtype=np.float32)
     rc = lib.oracle_fused_rows(ptrs, len(xs), _ptr(residual), _ptr(weight), _ptr(out),
@@ -154,6 +169,15 @@ def fp16_from_double(v) -> np.ndarray:
     o = np.empty(v.shape, dtype=np.uint16)
     _load().orc_fp16_from_double_n(_ptr(v), _ptr(o), v.size)
     return o
+
+
+def e2m1_from_float(v) -> np.ndarray:
+    """E2M1 codes (low nibble) of fp32 values, RNE, saturating to +-6."""
+    lib = _load()
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.zeros(v.shape, dtype=np.uint8)
+    lib.orc_e2m1_from_float_n(_ptr(v), _ptr(out), v.size)
+    return out
 
 
 def e4m3_from_float(v) -> np.ndarray:

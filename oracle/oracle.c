@@ -29,6 +29,16 @@
  *       q_j = E4M3_RNE_sat( fl32(y_j / scale) ) ; amax == 0 gives
  *       scale = 0 and q_j = signed zero.
  *
+ * The pages also name per-group and MXFP4 quant forms of the fused op
+ * (PR #6699 Motivation and Changes) without defining them; this oracle
+ * reads them as:
+ *   O6  per-group FP8: O5's steps on each group of 128 consecutive
+ *       columns (scales [M][H/128] fp32);
+ *   O7  MXFP4 (OCP Microscaling Formats v1.0, MXFP4): blocks of 32
+ *       columns, E8M0 scale X = 2^(floor(log2(amax)) - 2), elements
+ *       E2M1_RNE_sat(y / X), two per byte with the even column in the low
+ *       nibble (codes [M][H/2], scales [M][H/32] bytes).
+ *
  * For T = fp32 the RNE_T steps of O1/O2 are the fp32 operations
  * themselves and O4 rounds fp64 -> fp32 once.
  *
@@ -48,6 +58,10 @@
 #define ORC_DT_MASK 3
 #define ORC_GEMMA 4
 #define ORC_FP8 8
+#define ORC_FP8G 16        /* per-group FP8: scale per group of ORC_FP8_GROUP columns */
+#define ORC_MXFP4 32       /* MXFP4: E8M0 scale per block of ORC_MX_BLOCK columns, E2M1 elements */
+#define ORC_FP8_GROUP 128
+#define ORC_MX_BLOCK 32
 
 /* ------------------------------------------------------------------ */
 /* Rounding to p significant bits (round to nearest, ties to even).    */
@@ -160,6 +174,60 @@ uint8_t orc_e4m3_from_float(float x)
     return (uint8_t)(sign | (uint8_t)((lead + 7) << 3) | mant);
 }
 
+/* OCP FP4 E2M1 (the MX element format): 2 significant bits, emin = 0
+ * (normals 1, 1.5, 2, 3, 4, 6; the subnormal 0.5), no infinities or NaN.
+ * Finite values round to nearest, ties to even, and saturate to +-6. The
+ * code is S.EE.M in the low nibble. NaN and infinities are not defined by
+ * the format; here NaN maps to +-6's code like the infinities. */
+uint8_t orc_e2m1_from_float(float x)
+{
+    uint8_t sign = signbit(x) ? 0x8u : 0;
+    if (isnan(x) || isinf(x))
+        return (uint8_t)(sign | 0x7u);
+    double r = fabs(round_p((double)x, 2, 0));
+    if (r > 6.0)
+        r = 6.0;
+    if (r == 0.0)
+        return sign;
+    if (r < 1.0) /* the subnormal 0.5 */
+        return (uint8_t)(sign | 1u);
+    int e;
+    double f = frexp(r, &e); /* r = f * 2^e, f in [0.5, 1) */
+    uint8_t mant = (uint8_t)(ldexp(f, 2) - 2.0);
+    return (uint8_t)(sign | (uint8_t)(e << 1) | mant);
+}
+
+double orc_e2m1_to_double(uint8_t c)
+{
+    double s = (c & 0x8u) ? -1.0 : 1.0;
+    int ex = (c >> 1) & 3;
+    int m = c & 1;
+    if (ex == 0)
+        return s * 0.5 * m;
+    return s * ldexp(1.0 + 0.5 * m, ex - 1);
+}
+
+/* MX shared scale of a block (OCP Microscaling Formats v1.0, section 6.3):
+ * X = 2^(floor(log2(amax)) - emax_elem) with emax_elem = 2 for E2M1,
+ * returned as its E8M0 code (biased exponent, bias 127), the exponent
+ * clamped to [-127, 127]. An all-zero block takes 2^-127 (code 0); a block
+ * with a NaN or an infinity takes the E8M0 NaN code 0xFF. */
+uint8_t orc_mx_scale_code(float amax)
+{
+    if (isnan(amax) || isinf(amax))
+        return 0xFFu;
+    if (amax == 0.0f)
+        return 0;
+    int e;
+    frexp((double)amax, &e); /* floor(log2(amax)) = e - 1 */
+    int se = (e - 1) - 2;
+    if (se < -127)
+        se = -127;
+    if (se > 127)
+        se = 127;
+    return (uint8_t)(se + 127);
+}
+
 double orc_e4m3_to_double(uint8_t q)
 {
     double s = (q & 0x80u) ? -1.0 : 1.0;
@@ -227,9 +295,15 @@ int oracle_fused_rows(const void *const *rank_in, int R, const void *residual,
     int dt = flags & ORC_DT_MASK;
     int gemma = (flags & ORC_GEMMA) != 0;
     int fp8 = (flags & ORC_FP8) != 0;
+    int fp8g = (flags & ORC_FP8G) != 0;
+    int mx = (flags & ORC_MXFP4) != 0;
     if (R < 1 || H < 1 || M < 0 || dt > ORC_DT_FP32)
         return -1;
-    if (fp8 && (dt == ORC_DT_FP32 || !fp8_out || !fp8_scale))
+    if (fp8 + fp8g + mx > 1)
+        return -1;
+    if ((fp8 || fp8g || mx) && (dt == ORC_DT_FP32 || !fp8_out || !fp8_scale))
+        return -1;
+    if ((fp8g && H % ORC_FP8_GROUP) || (mx && H % ORC_MX_BLOCK))
         return -1;
     if (row_begin < 0 || row_end > M || row_begin > row_end)
         return -1;
@@ -282,6 +356,57 @@ int oracle_fused_rows(const void *const *rank_in, int R, const void *residual,
                     q[j] = signbit(y) ? 0x80u : 0x00u;
                 else
                     q[j] = orc_e4m3_from_float(y / scale); /* fp32 division */
+            }
+        }
+
+        /* per-group FP8: the per-token steps on each group of columns */
+        if (fp8g) {
+            int ng = H / ORC_FP8_GROUP;
+            uint8_t *q = (uint8_t *)fp8_out + row;
+            for (int g = 0; g < ng; ++g) {
+                const float *yg = h_scratch + (size_t)g * ORC_FP8_GROUP;
+                float gmax = 0.0f;
+                for (int j = 0; j < ORC_FP8_GROUP; ++j)
+                    if (fabsf(yg[j]) > gmax)
+                        gmax = fabsf(yg[j]);
+                float scale = gmax / 448.0f;
+                ((float *)fp8_scale)[(size_t)m * ng + g] = scale;
+                for (int j = 0; j < ORC_FP8_GROUP; ++j) {
+                    float y = yg[j];
+                    q[(size_t)g * ORC_FP8_GROUP + j] = gmax == 0.0f ? (signbit(y) ? 0x80u : 0x00u)
+                                                                     : orc_e4m3_from_float(y / scale);
+                }
+            }
+        }
+
+        /* MXFP4: E8M0 block scale, E2M1 elements of y / X (exact: X is a power
+         * of two), two per byte, the even column in the low nibble */
+        if (mx) {
+            int nb = H / ORC_MX_BLOCK;
+            uint8_t *q = (uint8_t *)fp8_out + (size_t)m * (size_t)(H / 2);
+            for (int b = 0; b < nb; ++b) {
+                const float *yb = h_scratch + (size_t)b * ORC_MX_BLOCK;
+                float bmax = 0.0f;
+                int bad = 0;
+                for (int j = 0; j < ORC_MX_BLOCK; ++j) {
+                    if (isnan(yb[j]))
+                        bad = 1;
+                    else if (fabsf(yb[j]) > bmax)
+                        bmax = fabsf(yb[j]);
+                }
+                uint8_t code = orc_mx_scale_code(bad ? NAN : bmax);
+                ((uint8_t *)fp8_scale)[(size_t)m * nb + b] = code;
+                for (int j = 0; j < ORC_MX_BLOCK; j += 2) {
+                    uint8_t c[2];
+                    for (int t = 0; t < 2; ++t) {
+                        float y = yb[j + t];
+                        if (code == 0xFFu)
+                            c[t] = (uint8_t)((signbit(y) ? 0x8u : 0) | 0x7u);
+                        else
+                            c[t] = orc_e2m1_from_float((float)ldexp((double)y, 127 - (int)code));
+                    }
+                    q[(size_t)(b * ORC_MX_BLOCK + j) / 2] = (uint8_t)(c[0] | (c[1] << 4));
+                }
             }
         }
     }
@@ -345,6 +470,12 @@ void orc_fp16_from_double_n(const double *v, uint16_t *out, size_t n)
 {
     for (size_t i = 0; i < n; ++i)
         out[i] = orc_fp16_from_double(v[i]);
+}
+
+void orc_e2m1_from_float_n(const float *v, uint8_t *out, size_t n)
+{
+    for (size_t i = 0; i < n; ++i)
+        out[i] = orc_e2m1_from_float(v[i]);
 }
 
 void orc_e4m3_from_float_n(const float *v, uint8_t *out, size_t n)

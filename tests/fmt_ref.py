@@ -31,6 +31,8 @@ BF16_VALUES = _decode_table(8, 7, 127, 0x7F7F)
 FP16_VALUES = _decode_table(5, 10, 15, 0x7BFF)
 # E4M3 "fn": 4 exponent bits, 3 fraction bits, bias 7; 0x7E = 448 (0x7F is NaN).
 E4M3_VALUES = _decode_table(4, 3, 7, 0x7E)
+# E2M1 (OCP MX FP4): 2 exponent bits, 1 fraction bit, bias 1; 0x7 = 6, no inf/NaN.
+E2M1_VALUES = _decode_table(2, 1, 1, 0x7)
 
 
 def nearest_code(v: np.ndarray, table: np.ndarray, overflow: str) -> np.ndarray:
@@ -78,6 +80,18 @@ def e4m3_bits(v) -> np.ndarray:
     v = np.asarray(v, dtype=np.float64)
     c = nearest_code(v, E4M3_VALUES, "sat").astype(np.uint8)
     return (c | np.where(np.signbit(v), 0x80, 0).astype(np.uint8)).astype(np.uint8)
+
+
+def e2m1_bits(v) -> np.ndarray:
+    v = np.asarray(v, dtype=np.float64)
+    c = nearest_code(v, E2M1_VALUES, "sat").astype(np.uint8)
+    return (c | np.where(np.signbit(v), 0x8, 0).astype(np.uint8)).astype(np.uint8)
+
+
+def e2m1_value(bits) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    mag = E2M1_VALUES[b & 0x7]
+    return np.where(b & 0x8, -mag, mag)
 
 
 def bf16_value(bits) -> np.ndarray:
