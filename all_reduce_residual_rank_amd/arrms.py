@@ -43,7 +43,12 @@ MAX_HIDDEN = 16384
 DEFAULT_STAGING_BYTES = 16 << 20
 PATH_NONE, PATH_ONE_STAGE, PATH_TWO_STAGE = 0, 1, 2
 
-EXPORTS = ("arrms_fused", "arrms_fused_strided", "arrms_allreduce_sum", "arrms_fused_config",
+QUANT_FP8_TOKEN, QUANT_FP8_GROUP, QUANT_MXFP4 = 1, 2, 3
+FP8_GROUP_SIZE = 128
+MX_BLOCK = 32
+
+EXPORTS = ("arrms_fused", "arrms_fused_strided", "arrms_fused_quant", "arrms_allreduce_sum",
+           "arrms_fused_config",
            "arrms_reserve_staging", "arrms_release_staging", "arrms_staging_bytes", "arrms_query_path",
            "arrms_status_string")
 
@@ -54,6 +59,9 @@ _lib.arrms_fused.restype = _i
 _lib.arrms_fused_strided.argtypes = [ctypes.POINTER(_vp), _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
                                      _ll, _ll, _ll, _ll, _ll, _f, _i, _vp]
 _lib.arrms_fused_strided.restype = _i
+_lib.arrms_fused_quant.argtypes = [ctypes.POINTER(_vp), _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i,
+                                   _i, _vp]
+_lib.arrms_fused_quant.restype = _i
 _lib.arrms_allreduce_sum.argtypes = [ctypes.POINTER(_vp), _i, _vp, _ll, _i, _vp]
 _lib.arrms_allreduce_sum.restype = _i
 _lib.arrms_fused_config.argtypes = [ctypes.POINTER(_vp), _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i,
@@ -192,6 +200,28 @@ def arrms_fused_strided(rank_in, residual, weight, out, residual_out, fp8_out=No
                                  eps, flags, _stream_handle(stream))
     if rc != OK:
         raise ArrmsError(rc, "arrms_fused_strided")
+
+
+def arrms_fused_quant_raw(rank_in, R, residual, weight, out, residual_out, q_out, q_scale, M, H, eps,
+                          flags, quant, stream) -> int:
+    """arrms_fused_quant with addresses as ints; returns the status unchanged."""
+    ptrs = (_vp * max(len(rank_in), 1))(*[_addr(p) for p in rank_in])
+    return _lib.arrms_fused_quant(ptrs, int(R), _addr(residual), _addr(weight), _addr(out),
+                                  _addr(residual_out), _addr(q_out), _addr(q_scale), int(M), int(H),
+                                  float(eps), int(flags), int(quant), stream)
+
+
+def arrms_fused_quant(rank_in, residual, weight, out, residual_out, q_out, q_scale, *, eps: float,
+                      flags: int, quant: int, M: int | None = None, H: int | None = None,
+                      stream=None) -> None:
+    """The fused epilogue with a quantised output (QUANT_FP8_TOKEN, QUANT_FP8_GROUP
+    or QUANT_MXFP4); ``out`` is the optional T mirror."""
+    if M is None or H is None:
+        M, H = residual.shape[-2], residual.shape[-1]
+    rc = arrms_fused_quant_raw(rank_in, len(rank_in), residual, weight, out, residual_out, q_out, q_scale,
+                               M, H, eps, flags, quant, _stream_handle(stream))
+    if rc != OK:
+        raise ArrmsError(rc, "arrms_fused_quant")
 
 
 def arrms_allreduce_sum_raw(rank_in, R, out, n, flags, stream) -> int:

@@ -48,9 +48,12 @@ uintptr_t span_bytes(int M, int H, long long ld, int e)
     return (uintptr_t)(M - 1) * (uintptr_t)ld * (uintptr_t)e + (uintptr_t)H * (uintptr_t)e;
 }
 
+// Quantised outputs: none, per-token FP8 (ARRMS_FP8), per-group FP8, MXFP4.
+enum Quant { Q_NONE = 0, Q_TOKEN = 1, Q_GROUP = 2, Q_MX = 3 };
+
 int validate(const void *const *rank_in, int R, const void *residual, const void *weight,
              const void *out, const void *residual_out, const void *fp8_out,
-             const float *fp8_scale, int M, int H, float eps, int flags, const Strides &ld)
+             const void *fp8_scale, int M, int H, float eps, int flags, const Strides &ld, int quant)
 {
     if (flags & ~kKnownFlags)
         return ARRMS_ERR_INVALID;
@@ -63,7 +66,9 @@ int validate(const void *const *rank_in, int R, const void *residual, const void
         return ARRMS_ERR_INVALID;
     if (!(eps >= 0.0f) || eps > 3.4028234e38f)  // rejects NaN, negative, +inf
         return ARRMS_ERR_INVALID;
-    const bool fp8 = (flags & ARRMS_FP8) != 0;
+    const bool fp8 = quant != Q_NONE;
+    if ((flags & ARRMS_FP8) && quant != Q_TOKEN)
+        return ARRMS_ERR_INVALID;
     if (!rank_in || !residual || !weight || !residual_out)
         return ARRMS_ERR_INVALID;
     for (int r = 0; r < R; ++r)
@@ -77,6 +82,8 @@ int validate(const void *const *rank_in, int R, const void *residual, const void
         return ARRMS_ERR_UNSUPPORTED;
     if (fp8 && dt == DT_FP32)
         return ARRMS_ERR_UNSUPPORTED;
+    if ((quant == Q_GROUP && H % ARRMS_FP8_GROUP_SIZE) || (quant == Q_MX && H % ARRMS_MX_BLOCK))
+        return ARRMS_ERR_UNSUPPORTED;
     if (((long long)H * esize(dt)) % 16 != 0)
         return ARRMS_ERR_UNSUPPORTED;
     for (int r = 0; r < R; ++r)
@@ -85,7 +92,7 @@ int validate(const void *const *rank_in, int R, const void *residual, const void
     if (!aligned16(residual) || !aligned16(weight) || !aligned16(residual_out) ||
         (out && !aligned16(out)))
         return ARRMS_ERR_UNSUPPORTED;
-    if (fp8 && (!aligned16(fp8_out) || ((uintptr_t)fp8_scale & 3u)))
+    if (fp8 && (!aligned16(fp8_out) || (quant != Q_MX && ((uintptr_t)fp8_scale & 3u))))
         return ARRMS_ERR_UNSUPPORTED;
     // strides: at least a row, rows 16-byte aligned
     const int e = esize(dt);
@@ -97,10 +104,12 @@ int validate(const void *const *rank_in, int R, const void *residual, const void
             return ARRMS_ERR_UNSUPPORTED;
     }
     if (fp8) {
-        // FP8 codes go out 8 bytes per pack: rows must start 8-byte aligned
-        if (ld.q < H)
+        // codes go out 8 bytes per pack (E4M3) or 4 (packed E2M1): rows must
+        // start aligned to that
+        const long long qrow = quant == Q_MX ? H / 2 : H;
+        if (ld.q < qrow)
             return ARRMS_ERR_INVALID;
-        if (ld.q % 8 != 0)
+        if (ld.q % (quant == Q_MX ? 4 : 8) != 0)
             return ARRMS_ERR_UNSUPPORTED;
     }
     const bool inplace = residual_out == residual;
@@ -123,8 +132,14 @@ int validate(const void *const *rank_in, int R, const void *residual, const void
     if (out)
         outs[nout++] = {(uintptr_t)out, (uintptr_t)out + span_bytes(M, H, ld.out, e)};
     if (fp8) {
-        outs[nout++] = {(uintptr_t)fp8_out, (uintptr_t)fp8_out + span_bytes(M, H, ld.q, 1)};
-        outs[nout++] = {(uintptr_t)fp8_scale, (uintptr_t)fp8_scale + (uintptr_t)M * 4u};
+        const int qrow = quant == Q_MX ? H / 2 : H;
+        uintptr_t sbytes = (uintptr_t)M * 4u;
+        if (quant == Q_GROUP)
+            sbytes = (uintptr_t)M * (uintptr_t)(H / ARRMS_FP8_GROUP_SIZE) * 4u;
+        else if (quant == Q_MX)
+            sbytes = (uintptr_t)M * (uintptr_t)(H / ARRMS_MX_BLOCK);
+        outs[nout++] = {(uintptr_t)fp8_out, (uintptr_t)fp8_out + span_bytes(M, qrow, ld.q, 1)};
+        outs[nout++] = {(uintptr_t)fp8_scale, (uintptr_t)fp8_scale + sbytes};
     }
     for (int o = 0; o < nout; ++o) {
         for (int i = 0; i < nin; ++i)
@@ -222,18 +237,26 @@ arrms::RowShape choose_shape(int P, int R, long long M, bool fp8)
     return best;
 }
 
-hipError_t launch_row(int dt, bool fp8, bool mirror, const arrms::RowArgs &a, int R,
+hipError_t launch_row(int dt, int quant, bool mirror, const arrms::RowArgs &a, int R,
                       const arrms::RowShape &s, hipStream_t st)
 {
     switch (dt) {
     case DT_BF16:
-        if (!fp8)
-            return arrms::launch_row_bf16_t(a, R, s, st);
-        return mirror ? arrms::launch_row_bf16_fp8t(a, R, s, st) : arrms::launch_row_bf16_fp8(a, R, s, st);
+        switch (quant) {
+        case Q_NONE: return arrms::launch_row_bf16_t(a, R, s, st);
+        case Q_TOKEN:
+            return mirror ? arrms::launch_row_bf16_fp8t(a, R, s, st) : arrms::launch_row_bf16_fp8(a, R, s, st);
+        case Q_GROUP: return arrms::launch_row_bf16_fp8g(a, R, s, st);
+        default: return arrms::launch_row_bf16_mx4(a, R, s, st);
+        }
     case DT_FP16:
-        if (!fp8)
-            return arrms::launch_row_fp16_t(a, R, s, st);
-        return mirror ? arrms::launch_row_fp16_fp8t(a, R, s, st) : arrms::launch_row_fp16_fp8(a, R, s, st);
+        switch (quant) {
+        case Q_NONE: return arrms::launch_row_fp16_t(a, R, s, st);
+        case Q_TOKEN:
+            return mirror ? arrms::launch_row_fp16_fp8t(a, R, s, st) : arrms::launch_row_fp16_fp8(a, R, s, st);
+        case Q_GROUP: return arrms::launch_row_fp16_fp8g(a, R, s, st);
+        default: return arrms::launch_row_fp16_mx4(a, R, s, st);
+        }
     default:
         return arrms::launch_row_fp32_t(a, R, s, st);
     }
@@ -396,11 +419,12 @@ bool apply_shape(const ShapeReq *req, int P, int R, long long M, arrms::RowShape
 }
 
 int fused_impl(const void *const *rank_in, int R, const void *residual, const void *weight,
-               void *out, void *residual_out, void *fp8_out, float *fp8_scale, int M, int H,
-               float eps, int flags, const Strides &ld, const ShapeReq *req, hipStream_t stream)
+               void *out, void *residual_out, void *fp8_out, void *fp8_scale, int M, int H,
+               float eps, int flags, const Strides &ld, const ShapeReq *req, hipStream_t stream,
+               int quant)
 {
     int rc = validate(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H,
-                      eps, flags, ld);
+                      eps, flags, ld, quant);
     if (rc != ARRMS_OK)
         return rc;
     const int path = choose_path(M, H, R, flags);
@@ -410,7 +434,9 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
     const int dt = flags & ARRMS_DTYPE_MASK;
     const int e = esize(dt);
     const int P = H * e / 16;
-    const bool fp8 = (flags & ARRMS_FP8) != 0;
+    const bool fp8 = quant != Q_NONE;  // any quantised output
+    const int qgroups = quant == Q_GROUP ? H / ARRMS_FP8_GROUP_SIZE : quant == Q_MX ? H / ARRMS_MX_BLOCK : 1;
+    const size_t scale_row = quant == Q_GROUP ? (size_t)qgroups * 4u : quant == Q_MX ? (size_t)qgroups : 4u;
 
     arrms::RowArgs a;
     memset(&a, 0, sizeof(a));
@@ -419,7 +445,9 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
     a.out = out;
     a.residual_out = residual_out;
     a.fp8_out = fp8 ? fp8_out : nullptr;
-    a.fp8_scale = fp8 ? fp8_scale : nullptr;
+    a.fp8_scale = quant == Q_TOKEN ? (float *)fp8_scale : nullptr;
+    a.q_scale = (quant == Q_GROUP || quant == Q_MX) ? fp8_scale : nullptr;
+    a.qgroups = qgroups;
     a.P = P;
     a.H = H;
     a.ld_in = ld.in * e;
@@ -440,7 +468,7 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
         if (s.ppt == 0 || !apply_shape(req, P, R, M, s))
             return ARRMS_ERR_UNSUPPORTED;
         a.tpr = s.tpr;
-        return launch_row(dt, fp8, out != nullptr, a, R, s, stream) == hipSuccess ? ARRMS_OK : ARRMS_ERR_HIP;
+        return launch_row(dt, quant, out != nullptr, a, R, s, stream) == hipSuccess ? ARRMS_OK : ARRMS_ERR_HIP;
     }
 
     // ---- two-stage: per row chunk, flat rank reduce into staging, then the
@@ -501,7 +529,10 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
         b.out = out ? (char *)out + (size_t)m0 * (size_t)a.ld_out : nullptr;
         if (fp8) {
             b.fp8_out = (char *)fp8_out + (size_t)m0 * (size_t)a.ld_q;
-            b.fp8_scale = fp8_scale + m0;
+            if (quant == Q_TOKEN)
+                b.fp8_scale = (float *)fp8_scale + m0;
+            else
+                b.q_scale = (char *)fp8_scale + (size_t)m0 * scale_row;
         }
         b.M = n;
         // the row pass takes the one-stage shape of the whole launch, so both paths
@@ -510,7 +541,7 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
         if (s.ppt == 0 || !apply_shape(req, P, R, n, s))
             return ARRMS_ERR_UNSUPPORTED;
         b.tpr = s.tpr;
-        if (launch_row(dt, fp8, out != nullptr, b, 1, s, stream) != hipSuccess)
+        if (launch_row(dt, quant, out != nullptr, b, 1, s, stream) != hipSuccess)
             return ARRMS_ERR_HIP;
     }
     return ARRMS_OK;
@@ -526,7 +557,7 @@ int arrms_fused(const void *const *rank_in, int R, const void *residual, const v
 {
     const Strides ld = {H, H, H, H, H};
     return fused_impl(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H, eps,
-                      flags, ld, nullptr, stream);
+                      flags, ld, nullptr, stream, (flags & ARRMS_FP8) ? Q_TOKEN : Q_NONE);
 }
 
 int arrms_fused_strided(const void *const *rank_in, int R, const void *residual, const void *weight,
@@ -537,7 +568,7 @@ int arrms_fused_strided(const void *const *rank_in, int R, const void *residual,
 {
     const Strides ld = {ld_in, ld_residual, ld_out, ld_residual_out, (flags & ARRMS_FP8) ? ld_fp8 : H};
     return fused_impl(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H, eps,
-                      flags, ld, nullptr, stream);
+                      flags, ld, nullptr, stream, (flags & ARRMS_FP8) ? Q_TOKEN : Q_NONE);
 }
 
 int arrms_fused_config(const void *const *rank_in, int R, const void *residual, const void *weight,
@@ -550,7 +581,19 @@ int arrms_fused_config(const void *const *rank_in, int R, const void *residual, 
     const ShapeReq req = {ppt, tpr, rows_per_block, blocks, load_window};
     const Strides ld = {H, H, H, H, H};
     return fused_impl(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H, eps,
-                      flags, ld, &req, stream);
+                      flags, ld, &req, stream, (flags & ARRMS_FP8) ? Q_TOKEN : Q_NONE);
+}
+
+int arrms_fused_quant(const void *const *rank_in, int R, const void *residual, const void *weight,
+                      void *out, void *residual_out, void *q_out, void *q_scale, int M, int H, float eps,
+                      int flags, int quant, hipStream_t stream)
+{
+    if (quant < ARRMS_QUANT_FP8_TOKEN || quant > ARRMS_QUANT_MXFP4 || (flags & ARRMS_FP8))
+        return ARRMS_ERR_INVALID;
+    const int q = quant == ARRMS_QUANT_FP8_TOKEN ? Q_TOKEN : quant == ARRMS_QUANT_FP8_GROUP ? Q_GROUP : Q_MX;
+    const Strides ld = {H, H, H, H, q == Q_MX ? H / 2 : H};
+    return fused_impl(rank_in, R, residual, weight, out, residual_out, q_out, q_scale, M, H, eps,
+                      q == Q_TOKEN ? (flags | ARRMS_FP8) : flags, ld, nullptr, stream, q);
 }
 
 int arrms_allreduce_sum(const void *const *rank_in, int R, void *out, long long n, int flags,

@@ -1,0 +1,11 @@
+// kern_bf16_mx4.hip -- row kernels for T = bf16 with the MXFP4 output (E8M0 scale per 32 columns, E2M1 codes).
+#include "kernels.hpp"
+
+namespace arrms {
+
+hipError_t launch_row_bf16_mx4(const RowArgs &a, int R, const RowShape &s, hipStream_t st)
+{
+    return row_launch_epi<DT_BF16, EPI_MX4>(a, R, s, st);
+}
+
+}  // namespace arrms

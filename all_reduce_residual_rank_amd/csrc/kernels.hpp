@@ -246,7 +246,9 @@ ARRMS_DEV void st16_nt(void *p, long long i, u32x4 v) { __builtin_nontemporal_st
 // drops their stores, and zeros add nothing to the sum of squares or the
 // maximum. EPI selects the epilogue: T output only, FP8 only, or FP8 with the
 // T mirror.
-enum Epilogue { EPI_T = 0, EPI_FP8 = 1, EPI_FP8_T = 2 };
+// EPI_FP8G: per-group FP8 (scale per 128 columns); EPI_MX4: MXFP4 (E8M0
+// scale per 32 columns, E2M1 codes). Both write the T mirror when out is set.
+enum Epilogue { EPI_T = 0, EPI_FP8 = 1, EPI_FP8_T = 2, EPI_FP8G = 3, EPI_MX4 = 4 };
 
 struct RowCtx {
     int lt;      // thread index within the row group
@@ -295,6 +297,11 @@ ARRMS_DEV void bstore(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
 ARRMS_DEV void bstore8(u32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kBufAuxNT);
+}
+
+ARRMS_DEV void bstore4(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kBufAuxNT);
 }
 
 // Phase 1 keeps at most W 16-byte loads of a thread in flight (a sliding
@@ -389,6 +396,121 @@ ARRMS_DEV void reduce_pack(const u32x4 (&x)[R + 1], const u32x4 &w, double gadd,
     }
 }
 
+// Per-token FP8 steps on 8 T values with their scale: q = E4M3_RNE_sat(fl32(y /
+// scale)). y * (1/scale) rounds like y / scale when it lies in the normal E4M3
+// range [2^-6, 464) and at least 4 fp32 ulps from an E4M3 tie: the 20 bits
+// below E4M3's mantissa, moved to the top of a word and offset, land at or
+// below 6 << 12 exactly when they are within 3 ulps of the halfway pattern
+// 0x80000. Elements that fail the test (rare) are recomputed alone by IEEE
+// division and the exact encoder; fast == false takes that path for all.
+ARRMS_DEV u32x2 quant8_e4m3(const float (&y)[8], float scale, float inv, bool fast)
+{
+    u32x2 q = {0u, 0u};
+    if (fast) {
+        float cq[8];
+        bool bad[8];
+        uint64_t anybad = 0;  // wave mask
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            cq[e] = y[e] * inv;
+            const float m = __builtin_fabsf(cq[e]);
+            const uint32_t t = (__float_as_uint(cq[e]) << 12) + 0x80003000u;
+            bad[e] = !(m >= 0x1p-6f) | !(m < 464.0f) | (t <= 0x6000u);
+            anybad |= __builtin_amdgcn_ballot_w64(bad[e]);
+        }
+        q.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[0], cq[1], 0, false);
+        q.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[2], cq[3], (int)q.x, true);
+        q.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[4], cq[5], 0, false);
+        q.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[6], cq[7], (int)q.y, true);
+        if (anybad != 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (__builtin_amdgcn_ballot_w64(bad[e]) != 0 && bad[e]) {
+                    const uint32_t b = e4m3_encode(y[e] / scale);
+                    const int sh = 8 * (e & 3);
+                    if (e < 4)
+                        q.x = (q.x & ~(0xffu << sh)) | (b << sh);
+                    else
+                        q.y = (q.y & ~(0xffu << sh)) | (b << sh);
+                }
+            }
+        }
+    } else {
+        uint32_t qb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            qb[e] = scale == 0.0f ? ((__float_as_uint(y[e]) >> 24) & 0x80u) : e4m3_encode(y[e] / scale);
+        q.x = qb[0] | (qb[1] << 8) | (qb[2] << 16) | (qb[3] << 24);
+        q.y = qb[4] | (qb[5] << 8) | (qb[6] << 16) | (qb[7] << 24);
+    }
+    return q;
+}
+
+// max |y| of 8 values as fp32 bits: for non-negative floats the integer order
+// is the float order, and a NaN (bits above the infinity's) wins
+ARRMS_DEV uint32_t absmax_bits(const float (&y)[8])
+{
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t b = __float_as_uint(y[e]) & 0x7fffffffu;
+        m = b > m ? b : m;
+    }
+    return m;
+}
+
+// max over aligned groups of N lanes (N = 4 or 16) by DPP within 16-lane rows;
+// every lane of a group ends with the group's maximum
+template <int N> ARRMS_DEV uint32_t group_max_u32(uint32_t v)
+{
+    uint32_t t = __builtin_amdgcn_update_dpp(0u, v, 0xB1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
+    v = t > v ? t : v;
+    t = __builtin_amdgcn_update_dpp(0u, v, 0x4E, 0xf, 0xf, false);           // quad_perm [2,3,0,1]
+    v = t > v ? t : v;
+    if constexpr (N == 16) {
+        t = __builtin_amdgcn_update_dpp(0u, v, 0x141, 0xf, 0xf, false);      // row_half_mirror
+        v = t > v ? t : v;
+        t = __builtin_amdgcn_update_dpp(0u, v, 0x140, 0xf, 0xf, false);      // row_mirror
+        v = t > v ? t : v;
+    }
+    return v;
+}
+
+// E8M0 code of an MX block scale from the block's max |y| bits (OCP
+// Microscaling Formats v1.0, section 6.3): 2^(floor(log2 amax) - 2) for E2M1,
+// the exponent clamped at -127 (zero and tiny blocks: code 0); a NaN or an
+// infinity in the block gives the E8M0 NaN code 0xFF.
+ARRMS_DEV uint32_t mx_scale_code(uint32_t am)
+{
+    if (am >= 0x7f800000u)
+        return 0xffu;
+    const uint32_t biased = am >> 23;  // floor(log2 amax) + 127 for normal amax
+    return biased >= 2u ? biased - 2u : 0u;
+}
+
+// E2M1 codes of 8 T values under the block scale: y / X exactly (X a power of
+// two), then round to nearest, ties to even, saturating at 6 -- counted as the
+// number of E2M1 decision points the magnitude passes (a tie goes up only when
+// the upper neighbour's code is even); packed two per byte, the even column in
+// the low nibble. A block with a NaN or an infinity gets +-6's code throughout.
+ARRMS_DEV uint32_t mx_pack8(const float (&y)[8], uint32_t code)
+{
+    const float f = __uint_as_float((254u - (code < 254u ? code : 253u)) << 23);  // 2^(127 - code)
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float a = __builtin_fabsf(y[e] * f);
+        uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+        if (code == 0xffu)
+            c = 7u;
+        c |= (__float_as_uint(y[e]) >> 28) & 0x8u;
+        word |= c << (4 * e);
+    }
+    return word;
+}
+
 // The rows of one block: row group g = blockIdx.x, then g + gridDim.x, ...
 // (with the default grid of one block per row group the loop runs once).
 template <int DT, int R, int PPT, int EPI, int WIN>
@@ -396,8 +518,9 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
 {
     using F = Fmt<DT>;
     constexpr int EPW = F::EPW;
-    constexpr bool FP8 = (EPI != EPI_T);
-    constexpr bool OUT_T = (EPI != EPI_FP8);
+    constexpr bool FP8 = (EPI == EPI_FP8 || EPI == EPI_FP8_T);  // per-token FP8
+    constexpr bool GROUPQ = (EPI == EPI_FP8G || EPI == EPI_MX4);
+    constexpr bool OUT_T = (EPI == EPI_T || EPI == EPI_FP8_T);   // GROUPQ: when out is set
     constexpr int NS = R + 1;        // input streams
     constexpr int NL = PPT * NS;     // loads per thread and row
     constexpr int W = WIN < NL ? WIN : NL;
@@ -497,7 +620,8 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
             asm volatile("" : "+v"(w[k]));
         }
         const __amdgpu_buffer_rsrc_t rout_t = out_stream(a.out, row, a.ld_out, rb, a.M);
-        const __amdgpu_buffer_rsrc_t rout_q = out_stream(a.fp8_out, row, a.ld_q, rb / 2, a.M);
+        const __amdgpu_buffer_rsrc_t rout_q =
+            out_stream(a.fp8_out, row, a.ld_q, EPI == EPI_MX4 ? rb / 4 : rb / 2, a.M);
         // a throttled row writes residual_out once the row is reduced: the
         // stores never count against the load window, and the row's reads
         // are over before its writes begin (measured faster on MI355X)
@@ -573,7 +697,10 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
             }
             if constexpr (OUT_T)
                 bstore(yv, rout_t, off);
-            if constexpr (FP8 && DT != DT_FP32) {
+            if constexpr (GROUPQ)
+                if (a.out)
+                    bstore(yv, rout_t, off);
+            if constexpr ((FP8 || GROUPQ) && DT != DT_FP32) {
                 float y[8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -582,53 +709,25 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
                     y[2 * i] = t[0];
                     y[2 * i + 1] = t[1];
                 }
-                u32x2 q = {0u, 0u};
-                if (qfast) {
-                    float cq[8];
-                    bool bad[8];
-                    uint64_t anybad = 0;  // wave mask, as for risk
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        cq[e] = y[e] * inv;
-                        // y * (1/scale) rounds like y / scale when it lies in the normal
-                        // E4M3 range [2^-6, 464) and at least 4 fp32 ulps from an E4M3
-                        // tie: the 20 bits below E4M3's mantissa, moved to the top of a
-                        // word and offset, land at or below 6 << 12 exactly when they are
-                        // within 3 ulps of the halfway pattern 0x80000
-                        const float m = __builtin_fabsf(cq[e]);
-                        const uint32_t t = (__float_as_uint(cq[e]) << 12) + 0x80003000u;
-                        bad[e] = !(m >= 0x1p-6f) | !(m < 464.0f) | (t <= 0x6000u);
-                        anybad |= __builtin_amdgcn_ballot_w64(bad[e]);
-                    }
-                    q.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[0], cq[1], 0, false);
-                    q.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[2], cq[3], (int)q.x, true);
-                    q.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[4], cq[5], 0, false);
-                    q.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[6], cq[7], (int)q.y, true);
-                    if (anybad != 0) {
-                        // rare: recompute just those elements, by division and the
-                        // exact encoder
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            if (__builtin_amdgcn_ballot_w64(bad[e]) != 0 && bad[e]) {
-                                const uint32_t b = e4m3_encode(y[e] / scale);
-                                const int sh = 8 * (e & 3);
-                                if (e < 4)
-                                    q.x = (q.x & ~(0xffu << sh)) | (b << sh);
-                                else
-                                    q.y = (q.y & ~(0xffu << sh)) | (b << sh);
-                            }
-                        }
-                    }
+                const int pack = c.lt + k * c.tpr;  // pack index in the row
+                if constexpr (FP8) {
+                    bstore8(quant8_e4m3(y, scale, inv, qfast), rout_q, off / 2u);
+                } else if constexpr (EPI == EPI_FP8G) {
+                    // group max over the 16 lanes holding a group's 16 packs
+                    const float gmax = __uint_as_float(group_max_u32<16>(absmax_bits(y)));
+                    const float gscale = gmax / 448.0f;
+                    const bool gfast = !exact_only && gscale >= 1.17549435e-38f && gscale <= 3.0e38f;
+                    bstore8(quant8_e4m3(y, gscale, 1.0f / gscale, gfast), rout_q, off / 2u);
+                    if ((pack & 15) == 0 && pack < c.P && row < a.M)
+                        ((float *)a.q_scale)[row * a.qgroups + (pack >> 4)] = gscale;
                 } else {
-                    uint32_t qb[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        qb[e] = scale == 0.0f ? ((__float_as_uint(y[e]) >> 24) & 0x80u)
-                                              : e4m3_encode(y[e] / scale);
-                    q.x = qb[0] | (qb[1] << 8) | (qb[2] << 16) | (qb[3] << 24);
-                    q.y = qb[4] | (qb[5] << 8) | (qb[6] << 16) | (qb[7] << 24);
+                    // MXFP4: block max over the 4 lanes holding a block's 4 packs
+                    const uint32_t am = group_max_u32<4>(absmax_bits(y));
+                    const uint32_t code = mx_scale_code(am);
+                    bstore4(mx_pack8(y, code), rout_q, off / 4u);
+                    if ((pack & 3) == 0 && pack < c.P && row < a.M)
+                        ((uint8_t *)a.q_scale)[row * a.qgroups + (pack >> 2)] = (uint8_t)code;
                 }
-                bstore8(q, rout_q, off / 2u);
             }
         }
     }

@@ -21,8 +21,10 @@ struct RowArgs {
     const void *weight;
     void *out;            // may be null when fp8 is set (no T mirror)
     void *residual_out;
-    void *fp8_out;        // bytes, [M][H]
-    float *fp8_scale;     // [M]
+    void *fp8_out;        // bytes: E4M3 [M][H], or packed E2M1 [M][H/2]
+    float *fp8_scale;     // per-token FP8: [M]
+    void *q_scale;        // per-group FP8: fp32 [M][qgroups]; MXFP4: E8M0 bytes [M][qgroups]
+    int qgroups;          // quant groups per row (H / 128 or H / 32)
     long long M;          // rows
     int P;                // 16-byte packs per row
     // row strides in bytes: rank inputs, residual, out, residual_out, fp8 codes
@@ -85,6 +87,10 @@ hipError_t launch_row_fp16_t(const RowArgs &a, int R, const RowShape &s, hipStre
 hipError_t launch_row_fp16_fp8(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
 hipError_t launch_row_fp16_fp8t(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
 hipError_t launch_row_fp32_t(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
+hipError_t launch_row_bf16_fp8g(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
+hipError_t launch_row_bf16_mx4(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
+hipError_t launch_row_fp16_fp8g(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
+hipError_t launch_row_fp16_mx4(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
 hipError_t launch_flat_bf16(const FlatArgs &a, int R, hipStream_t st);
 hipError_t launch_flat_fp16(const FlatArgs &a, int R, hipStream_t st);
 hipError_t launch_flat_fp32(const FlatArgs &a, int R, hipStream_t st);

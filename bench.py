@@ -13,6 +13,8 @@ Prints one JSON line:
               residual read, out and residual_out written, the weight) over the
               measured kernel duration, against MI355X's 8 TB/s HBM peak
   cpu_baseline  the CPU oracle, single-threaded, on the same workload
+  quant_epilogues  per-token FP8, per-group FP8 and MXFP4 outputs on the FP8
+              workload's rows (R=4, 2800 x 6144 fp16, gemma_norm)
   allreduce_sum the plain rank all-reduce (no norm) over a message of the same
               rank inputs' size (4 x 1024 x 6144 bf16), with its own roofline
               fraction; --sum-only prints that measurement as the line instead
@@ -52,6 +54,8 @@ def parse():
     p.add_argument("--no-sum", action="store_true",
                    help="skip the plain rank all-reduce (no norm) timing")
     p.add_argument("--no-strided", action="store_true", help="skip the padded-rows timing")
+    p.add_argument("--no-quant", action="store_true",
+                   help="skip the per-token / per-group FP8 / MXFP4 epilogue timings")
     p.add_argument("--replays", type=int, default=20,
                    help="further timed replays of the chosen path, for median/min (0: none)")
     p.add_argument("--sum-only", action="store_true",
@@ -194,6 +198,38 @@ def time_strided(torch, arrms, wl, pad, steps, warmup):
     ms = time_graph(torch, calls, steps, warmup)
     del sets
     return ms * 1000.0 / steps
+
+
+def time_quant(torch, arrms, wl, quant, steps, warmup):
+    """The workload with a quantised output through arrms_fused_quant (no T
+    mirror). Returns (us per call, algorithmic bytes per call)."""
+    from all_reduce_residual_rank_amd import workloads as wlmod
+    dev = torch.device("cuda")
+    T = wlmod.DTYPES[wl.dtype]
+    e = wl.esize
+    M, H = wl.M, wl.H
+    if quant == arrms.QUANT_FP8_TOKEN:
+        qbytes, sbytes = M * H, M * 4
+    elif quant == arrms.QUANT_FP8_GROUP:
+        qbytes, sbytes = M * H, M * (H // arrms.FP8_GROUP_SIZE) * 4
+    else:
+        qbytes, sbytes = M * H // 2, M * (H // arrms.MX_BLOCK)
+    algo = (wl.R + 2) * M * H * e + H * e + qbytes + sbytes
+    xs, res, w = wlmod.make_inputs(wl, seed=0)
+    nsets = max(2, -(-ROTATE_BYTES // algo))
+    sets = [{"xs": [x.to(dev) for x in xs], "res": res.to(dev), "w": w.to(dev),
+             "rout": torch.empty(M, H, dtype=T, device=dev),
+             "q": torch.empty(qbytes, dtype=torch.uint8, device=dev),
+             "s": torch.empty(sbytes, dtype=torch.uint8, device=dev)} for _ in range(nsets)]
+    flags = (wl.flags & ~arrms.FP8) | arrms.FORCE_ONE_STAGE
+
+    def one(d, st):
+        arrms.arrms_fused_quant(d["xs"], d["res"], d["w"], None, d["rout"], d["q"], d["s"], eps=wl.eps,
+                                flags=flags, quant=quant, M=M, H=H, stream=st)
+
+    ms = time_graph(torch, [lambda st, d=d: one(d, st) for d in sets], steps, warmup)
+    del sets
+    return ms * 1000.0 / steps, algo
 
 
 def time_sum(torch, arrms, case, R, steps, warmup):
@@ -420,6 +456,18 @@ def main():
                            "achieved": round(algo_bytes / (st_us * 1e-6) / 1e9, 2), "unit": "GB/s",
                            "frac": round(algo_bytes / (st_us * 1e-6) / 1e9 / PEAK_GBS, 4),
                            "kernel": "row_kernel"}
+    if not args.no_quant:
+        # the quant forms of the epilogue on the FP8 workload's rows (R=4,
+        # 2800 x 6144 fp16, gemma_norm, no T mirror)
+        qwl = wlmod.FP8_GEMMA
+        qres = {}
+        for name, qm in (("per_token_fp8", arrms.QUANT_FP8_TOKEN), ("per_group_fp8", arrms.QUANT_FP8_GROUP),
+                         ("mxfp4", arrms.QUANT_MXFP4)):
+            q_us, q_bytes = time_quant(torch, arrms, qwl, qm, args.steps, args.warmup)
+            qres[name] = {"us_per_call": round(q_us, 3), "algorithmic_bytes": q_bytes,
+                          "achieved": round(q_bytes / (q_us * 1e-6) / 1e9, 2),
+                          "frac": round(q_bytes / (q_us * 1e-6) / 1e9 / PEAK_GBS, 4)}
+        line["quant_epilogues"] = {"workload": qwl.name, "unit": "GB/s", "kernel": "row_kernel", **qres}
     clocks = read_clocks()
     if clocks:
         line["clocks"] = clocks

@@ -51,6 +51,13 @@ extern "C" {
 #define ARRMS_EXACT_ONLY 64        /* verification: take the exact rounding branch for every element
                                       (same results; used to check the fast branches bit for bit) */
 
+/* ---- quantised outputs of arrms_fused_quant ------------------------------- */
+#define ARRMS_QUANT_FP8_TOKEN 1    /* per-token FP8: as arrms_fused with ARRMS_FP8 */
+#define ARRMS_QUANT_FP8_GROUP 2    /* per-group FP8: E4M3 codes [M][H], fp32 scales [M][H/128] */
+#define ARRMS_QUANT_MXFP4 3        /* MXFP4: packed E2M1 codes [M][H/2], E8M0 scales [M][H/32] */
+#define ARRMS_FP8_GROUP_SIZE 128   /* columns per per-group FP8 scale */
+#define ARRMS_MX_BLOCK 32          /* columns per MXFP4 scale (OCP MX block size) */
+
 /* ---- limits -------------------------------------------------------------- */
 #define ARRMS_MAX_RANKS 8          /* the pages go up to TP8 (PR #3462 Test Results) */
 #define ARRMS_MAX_HIDDEN 16384
@@ -133,6 +140,35 @@ ARRMS_API int arrms_fused_strided(const void *const *rank_in, int R, const void 
                                   float *fp8_scale, int M, int H, long long ld_in,
                                   long long ld_residual, long long ld_out, long long ld_residual_out,
                                   long long ld_fp8, float eps, int flags, hipStream_t stream);
+
+/*
+ * arrms_fused_quant -- arrms_fused with one of the quantised outputs the pages
+ * name for the fused op (PR #6699 Motivation and Changes: the per-token, the
+ * per-group and the MXFP4 quant forms). The pages do not define the last two;
+ * this library reads them as:
+ *   ARRMS_QUANT_FP8_GROUP  the per-token FP8 steps on each group of
+ *       ARRMS_FP8_GROUP_SIZE (128) consecutive columns: scale = fl32(gmax /
+ *       448) over the T-rounded y of the group, q = E4M3_RNE_sat(fl32(y /
+ *       scale)), an all-zero group gives scale 0 and signed zeros.
+ *       q_out: [M][H] E4M3 codes; q_scale: [M][H/128] fp32 (4-byte aligned).
+ *   ARRMS_QUANT_MXFP4  OCP Microscaling Formats v1.0 MXFP4 over blocks of
+ *       ARRMS_MX_BLOCK (32) columns: X = 2^(floor(log2 bmax) - 2) with the
+ *       exponent clamped to [-127, 127], stored as its E8M0 code (an all-zero
+ *       block gives code 0; a NaN or an infinity in the block gives 0xFF and
+ *       +-6's element code); elements E2M1_RNE_sat(y / X) (y / X is exact).
+ *       q_out: [M][H/2] bytes, two codes per byte, the even column in the
+ *       low nibble (sign in bit 3 of each nibble); q_scale: [M][H/32] bytes.
+ *   ARRMS_QUANT_FP8_TOKEN  exactly arrms_fused with ARRMS_FP8 (q_scale [M] fp32).
+ * out is the optional T mirror (NULL: not written). H must be a multiple of
+ * the group (else ARRMS_ERR_UNSUPPORTED), T bf16 or fp16; flags as for
+ * arrms_fused but without ARRMS_FP8 (ARRMS_ERR_INVALID), quant outside 1..3
+ * is ARRMS_ERR_INVALID. Rows are contiguous. Both paths, the results'
+ * determinism and every other rule are arrms_fused's.
+ */
+ARRMS_API int arrms_fused_quant(const void *const *rank_in, int R, const void *residual,
+                                const void *weight, void *out, void *residual_out, void *q_out,
+                                void *q_scale, int M, int H, float eps, int flags, int quant,
+                                hipStream_t stream);
 
 /*
  * arrms_allreduce_sum -- the plain rank all-reduce without the norm epilogue

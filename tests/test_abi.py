@@ -51,7 +51,8 @@ def test_binding_constants_match_header():
     for name in ("OK", "ERR_INVALID", "ERR_UNSUPPORTED", "ERR_NO_STAGING", "ERR_HIP", "DTYPE_BF16",
                  "DTYPE_FP16", "DTYPE_FP32", "GEMMA", "FP8", "FORCE_ONE_STAGE", "FORCE_TWO_STAGE",
                  "EXACT_ONLY", "MAX_RANKS", "MAX_HIDDEN", "PATH_NONE", "PATH_ONE_STAGE",
-                 "PATH_TWO_STAGE"):
+                 "PATH_TWO_STAGE", "QUANT_FP8_TOKEN", "QUANT_FP8_GROUP", "QUANT_MXFP4",
+                 "FP8_GROUP_SIZE", "MX_BLOCK"):
         assert getattr(arrms, name) == c[name], name
 
 
@@ -211,3 +212,36 @@ def test_fused_config_argument_checks():
         ppt, tpr, rpb, blocks, win = bad
         assert arrms.arrms_fused_config_raw(*args, ppt, tpr, rpb, blocks, None, load_window=win) == \
             arrms.ERR_INVALID, bad
+
+
+def _quant(R=4, M=8, H=256, flags=0, quant=2, eps=1e-6, **over):
+    ptr = {f"in{r}": BASE + r * STRIDE for r in range(8)}
+    ptr.update(residual=BASE + 10 * STRIDE, weight=BASE + 11 * STRIDE, out=None,
+               residual_out=BASE + 13 * STRIDE, q_out=BASE + 14 * STRIDE, q_scale=BASE + 15 * STRIDE)
+    ptr.update(over)
+    return arrms.arrms_fused_quant_raw([ptr[f"in{r}"] for r in range(R)], R, ptr["residual"], ptr["weight"],
+                                       ptr["out"], ptr["residual_out"], ptr["q_out"], ptr["q_scale"], M, H,
+                                       eps, flags, quant, None)
+
+
+def test_fused_quant_argument_checks():
+    for q in (1, 2, 3):
+        assert _quant(M=0, quant=q) == arrms.OK
+        assert _quant(M=0, quant=q, flags=arrms.DTYPE_FP16 | arrms.GEMMA) == arrms.OK
+    for kw in (dict(quant=0), dict(quant=4), dict(flags=arrms.FP8), dict(q_out=None), dict(q_scale=None),
+               dict(residual_out=None)):
+        assert _quant(**kw) == arrms.ERR_INVALID, kw
+    # group sizes: per-group FP8 needs H % 128, MXFP4 H % 32; fp32 has no quant forms
+    assert _quant(H=192, quant=2) == arrms.ERR_UNSUPPORTED
+    assert _quant(M=0, H=192, quant=3) == arrms.OK
+    assert _quant(H=80, quant=3) == arrms.ERR_UNSUPPORTED
+    assert _quant(quant=2, flags=arrms.DTYPE_FP32) == arrms.ERR_UNSUPPORTED
+    # MXFP4 scales are bytes: any alignment; FP8 group scales are fp32: 4-byte aligned
+    assert _quant(M=0, quant=3, q_scale=BASE + 15 * STRIDE + 1) == arrms.OK
+    assert _quant(quant=2, q_scale=BASE + 15 * STRIDE + 2) == arrms.ERR_UNSUPPORTED
+    # overlap: the group scales [M][H/128] fp32 run into the codes
+    M, H = 8, 256
+    assert _quant(quant=2, q_scale=BASE + 14 * STRIDE + M * H - 4) == arrms.ERR_INVALID
+    assert _quant(M=0, quant=2, q_scale=BASE + 14 * STRIDE + M * H) == arrms.OK
+    # MXFP4 codes are [M][H/2]: scales right after them do not overlap
+    assert _quant(M=0, quant=3, q_scale=BASE + 14 * STRIDE + M * H // 2) == arrms.OK
