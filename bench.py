@@ -270,26 +270,24 @@ def time_hot(torch, arrms, wl, sets, flags, reps=64):
     return min(res)
 
 
-def read_clocks():
-    """Current shader and memory clocks from a read-only rocm-smi query, if it
-    answers within a few seconds; else None."""
-    import subprocess
+def read_clocks(torch):
+    """Current shader and memory clocks of device 0, read from the amdgpu
+    driver's sysfs DPM tables (the entry marked with '*'); None where the files
+    are not readable. A file read, so nothing is spawned from this process."""
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
-                           timeout=10)
-        d = json.loads(r.stdout)
-    except (OSError, ValueError, subprocess.SubprocessError):
-        return None
-    card = next((v for k, v in d.items() if k.startswith("card")), None)
-    if not isinstance(card, dict):
+        p = torch.cuda.get_device_properties(0)
+        root = "/sys/bus/pci/devices/%04x:%02x:%02x.0" % (p.pci_domain_id, p.pci_bus_id, p.pci_device_id)
+    except (AttributeError, RuntimeError):
         return None
     out = {}
-    for key, val in card.items():
-        k = key.lower()
-        if "sclk" in k and "mhz" in str(val).lower():
-            out["sclk"] = val
-        elif "mclk" in k and "mhz" in str(val).lower():
-            out["mclk"] = val
+    for key, name in (("sclk", "pp_dpm_sclk"), ("mclk", "pp_dpm_mclk")):
+        try:
+            with open(os.path.join(root, name)) as f:
+                cur = [ln.split(":", 1)[1].replace("*", "").strip() for ln in f if ln.rstrip().endswith("*")]
+        except (OSError, IndexError):
+            continue
+        if cur:
+            out[key] = cur[0]
     return out or None
 
 
@@ -468,7 +466,7 @@ def main():
                           "achieved": round(q_bytes / (q_us * 1e-6) / 1e9, 2),
                           "frac": round(q_bytes / (q_us * 1e-6) / 1e9 / PEAK_GBS, 4)}
         line["quant_epilogues"] = {"workload": qwl.name, "unit": "GB/s", "kernel": "row_kernel", **qres}
-    clocks = read_clocks()
+    clocks = read_clocks(torch)
     if clocks:
         line["clocks"] = clocks
     if not args.no_cpu_baseline:
