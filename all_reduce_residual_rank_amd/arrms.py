@@ -40,6 +40,7 @@ FORCE_TWO_STAGE = 32
 EXACT_ONLY = 64
 MAX_RANKS = 8
 MAX_HIDDEN = 16384
+MAX_ROW_BYTES = 32768
 DEFAULT_STAGING_BYTES = 16 << 20
 PATH_NONE, PATH_ONE_STAGE, PATH_TWO_STAGE = 0, 1, 2
 

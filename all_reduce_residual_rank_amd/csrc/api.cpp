@@ -36,7 +36,6 @@ struct Span {
 
 bool overlaps(const Span &a, const Span &b) { return a.lo < b.hi && b.lo < a.hi; }
 
-// Checks that need no device: sizes, flags, pointers, alignment, overlap.
 // Row strides of the fused call, in elements of each tensor (fp8: bytes).
 struct Strides {
     long long in, res, out, rout, q;
@@ -51,6 +50,7 @@ uintptr_t span_bytes(int M, int H, long long ld, int e)
 // Quantised outputs: none, per-token FP8 (ARRMS_FP8), per-group FP8, MXFP4.
 enum Quant { Q_NONE = 0, Q_TOKEN = 1, Q_GROUP = 2, Q_MX = 3 };
 
+// Checks that need no device: sizes, flags, pointers, alignment, overlap.
 int validate(const void *const *rank_in, int R, const void *residual, const void *weight,
              const void *out, const void *residual_out, const void *fp8_out,
              const void *fp8_scale, int M, int H, float eps, int flags, const Strides &ld, int quant)
@@ -84,7 +84,7 @@ int validate(const void *const *rank_in, int R, const void *residual, const void
         return ARRMS_ERR_UNSUPPORTED;
     if ((quant == Q_GROUP && H % ARRMS_FP8_GROUP_SIZE) || (quant == Q_MX && H % ARRMS_MX_BLOCK))
         return ARRMS_ERR_UNSUPPORTED;
-    if (((long long)H * esize(dt)) % 16 != 0)
+    if (((long long)H * esize(dt)) % 16 != 0 || (long long)H * esize(dt) > ARRMS_MAX_ROW_BYTES)
         return ARRMS_ERR_UNSUPPORTED;
     for (int r = 0; r < R; ++r)
         if (!aligned16(rank_in[r]))
@@ -170,7 +170,7 @@ int validate_sizes(int M, int H, int R, int flags)
         return ARRMS_ERR_UNSUPPORTED;
     if ((flags & ARRMS_FP8) && dt == DT_FP32)
         return ARRMS_ERR_UNSUPPORTED;
-    if (((long long)H * esize(dt)) % 16 != 0)
+    if (((long long)H * esize(dt)) % 16 != 0 || (long long)H * esize(dt) > ARRMS_MAX_ROW_BYTES)
         return ARRMS_ERR_UNSUPPORTED;
     return ARRMS_OK;
 }
@@ -321,7 +321,7 @@ const char *arrms_status_string(int status)
     case ARRMS_OK: return "ok";
     case ARRMS_ERR_INVALID: return "invalid argument (pointer, size, flags or overlap)";
     case ARRMS_ERR_UNSUPPORTED:
-        return "unsupported layout (alignment, H*sizeof(T) % 16, FP8 with fp32, H too large)";
+        return "unsupported layout (alignment, H*sizeof(T) % 16, FP8 with fp32, row too wide)";
     case ARRMS_ERR_NO_STAGING: return "two-stage path inside stream capture without reserved staging";
     case ARRMS_ERR_HIP: return "HIP runtime or launch error";
     default: return "unknown status";

@@ -1,5 +1,6 @@
 // kernels.hpp -- gfx950 kernels of the fused rank-sum + residual-add + RMSNorm
-// (+ per-token FP8 E4M3) epilogue. Included by the per-dtype translation units.
+// epilogue (+ per-token or per-group FP8 E4M3, or MXFP4) and of the plain rank
+// sum. Included by the per-dtype, per-epilogue translation units.
 //
 // Numerics (ROCm/aiter PR #6699 "gfx1250 fused all-reduce + RMSNorm", section
 // Changes; PR #3462 "optimize fused AllReduce + RMSNorm", section Technical
@@ -221,7 +222,6 @@ ARRMS_DEV double wave_max_f64(double v)
 // not for its outstanding global loads and stores.
 ARRMS_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-ARRMS_DEV u32x4 ld16(const void *p, long long i) { return ((const u32x4 *)p)[i]; }
 ARRMS_DEV void st16(void *p, long long i, u32x4 v) { ((u32x4 *)p)[i] = v; }
 // Streaming (read-once / write-once) data: non-temporal accesses, so the rank
 // inputs and the outputs do not displace the reused lines (weights) in the

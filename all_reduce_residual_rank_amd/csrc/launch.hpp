@@ -1,6 +1,6 @@
-// launch.hpp -- internal interface between the C ABI (api.cpp) and the
-// per-dtype kernel translation units (kern_bf16.hip, kern_fp16.hip,
-// kern_fp32.hip). Not installed; not part of the public header.
+// launch.hpp -- internal interface between the C ABI (api.cpp) and the kernel
+// translation units (kern_<dtype>_<epilogue>.hip, one per dtype and epilogue).
+// Not installed; not part of the public header.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -38,7 +38,8 @@ struct RowArgs {
     int exact_only;
 };
 
-// Arguments of the flat rank reduce (stage 1 of two-stage).
+// Arguments of the flat rank reduce (stage 1 of two-stage, and the plain rank
+// all-reduce).
 // The reduced region is rows x P packs: row m of rank r starts at pack
 // m * ld_in of in[r] and lands at pack m * ld_out of dst. Contiguous data is
 // one row of all its packs.
@@ -79,7 +80,9 @@ constexpr int kFlatWindow = ARRMS_FLAT_WINDOW;  // 16-byte loads in flight per t
 constexpr int kFlatTile = kFlatThreads * kFlatPacksPerThread;
 
 // Row kernels, one entry per dtype and epilogue (kern_<dtype>_<epilogue>.hip):
-// _t writes the T output, _fp8 the FP8 output only, _fp8t FP8 plus the T mirror.
+// _t writes the T output, _fp8 the per-token FP8 output only, _fp8t per-token
+// FP8 plus the T mirror, _fp8g per-group FP8 and _mx4 MXFP4 (each with the T
+// mirror when out is set).
 hipError_t launch_row_bf16_t(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
 hipError_t launch_row_bf16_fp8(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
 hipError_t launch_row_bf16_fp8t(const RowArgs &a, int R, const RowShape &s, hipStream_t st);

@@ -61,6 +61,7 @@ extern "C" {
 /* ---- limits -------------------------------------------------------------- */
 #define ARRMS_MAX_RANKS 8          /* the pages go up to TP8 (PR #3462 Test Results) */
 #define ARRMS_MAX_HIDDEN 16384
+#define ARRMS_MAX_ROW_BYTES 32768 /* H * sizeof(T): a row is at most 2048 packs (fp32: H <= 8192) */
 #define ARRMS_DEFAULT_STAGING_BYTES (16u << 20) /* 16 MiB staging region (PR #6699 Changes) */
 
 /* ---- paths returned by arrms_query_path ---------------------------------- */
@@ -98,7 +99,8 @@ extern "C" {
  * fp8_out      device [M][H] bytes (E4M3 codes), required with ARRMS_FP8, else ignored.
  * fp8_scale    device [M] float, required with ARRMS_FP8, else ignored.
  * M            rows, >= 0 (0: returns ARRMS_OK, launches nothing).
- * H            hidden size, 1 .. ARRMS_MAX_HIDDEN, with H * sizeof(T) % 16 == 0.
+ * H            hidden size, 1 .. ARRMS_MAX_HIDDEN, with H * sizeof(T) % 16 == 0 and
+ *              H * sizeof(T) <= ARRMS_MAX_ROW_BYTES.
  * eps          finite, >= 0.
  * flags        ARRMS_DTYPE_* | ARRMS_GEMMA | ARRMS_FP8 | at most one ARRMS_FORCE_* |
  *              ARRMS_EXACT_ONLY. ARRMS_FP8 requires bf16 or fp16.

@@ -50,7 +50,7 @@ def test_binding_constants_match_header():
     c = header_constants()
     for name in ("OK", "ERR_INVALID", "ERR_UNSUPPORTED", "ERR_NO_STAGING", "ERR_HIP", "DTYPE_BF16",
                  "DTYPE_FP16", "DTYPE_FP32", "GEMMA", "FP8", "FORCE_ONE_STAGE", "FORCE_TWO_STAGE",
-                 "EXACT_ONLY", "MAX_RANKS", "MAX_HIDDEN", "PATH_NONE", "PATH_ONE_STAGE",
+                 "EXACT_ONLY", "MAX_RANKS", "MAX_HIDDEN", "MAX_ROW_BYTES", "PATH_NONE", "PATH_ONE_STAGE",
                  "PATH_TWO_STAGE", "QUANT_FP8_TOKEN", "QUANT_FP8_GROUP", "QUANT_MXFP4",
                  "FP8_GROUP_SIZE", "MX_BLOCK"):
         assert getattr(arrms, name) == c[name], name
@@ -94,6 +94,7 @@ def test_invalid_arguments(kw):
     dict(H=60),                                  # 120 bytes per bf16 row: not 16-byte packs
     dict(H=6, flags=arrms.DTYPE_FP32),           # 24 bytes per fp32 row
     dict(H=arrms.MAX_HIDDEN + 8),
+    dict(H=arrms.MAX_ROW_BYTES // 4 + 4, flags=arrms.DTYPE_FP32),  # fp32 row past 32 KiB
     dict(flags=arrms.DTYPE_FP32 | arrms.FP8),
     dict(in1=BASE + STRIDE + 8),                 # misaligned rank input
     dict(residual=BASE + 10 * STRIDE + 2),
@@ -132,6 +133,10 @@ def test_query_path():
     assert arrms.arrms_query_path(1024, 60, 4, 0) == arrms.ERR_UNSUPPORTED
     assert arrms.arrms_query_path(1024, 64, 9, 0) == arrms.ERR_INVALID
     assert arrms.arrms_query_path(16, 512, 4, arrms.DTYPE_FP32 | arrms.FP8) == arrms.ERR_UNSUPPORTED
+    # rows are capped at 32 KiB: bf16 up to the hidden cap, fp32 up to 8192
+    assert arrms.arrms_query_path(16, 16384, 4, 0) == arrms.PATH_ONE_STAGE
+    assert arrms.arrms_query_path(16, 8192, 4, arrms.DTYPE_FP32) == arrms.PATH_ONE_STAGE
+    assert arrms.arrms_query_path(16, 8196, 4, arrms.DTYPE_FP32) == arrms.ERR_UNSUPPORTED
 
 
 def _call_strided(R=4, M=8, H=64, flags=0, eps=1e-6, ld=(64, 64, 64, 64, 64), **over):

@@ -129,6 +129,13 @@ def test_hidden_sizes_and_tails(H):
     _case(wl, 5, ("one", "two"))
 
 
+@pytest.mark.parametrize("H", [8188, 8192])
+def test_widest_fp32_rows(H):
+    # fp32 rows up to the 32 KiB row cap (2048 packs), ragged and exact
+    wl = wlmod.Workload("fp32wide", R=4, M=11, H=H, dtype="fp32", gemma=True, w_mean=0.0)
+    _case(wl, 9, ("one", "two"))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
 def test_exact_integer_sums(dtype):
     # the exact-integer generator of PR #5807's reproducer at its tail neighbours
