@@ -518,7 +518,6 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
         f.ld_in = a.ld_in / 16;
         f.ld_out = P;
         f.tiles = (f.P + arrms::kFlatTile - 1) / arrms::kFlatTile;
-        f.nt_store = 0;  // the row pass reads the staging rows right away
         if (launch_flat(dt, f, R, stream) != hipSuccess)
             return ARRMS_ERR_HIP;
         arrms::RowArgs b = a;
@@ -635,7 +634,6 @@ int arrms_allreduce_sum(const void *const *rank_in, int R, void *out, long long 
     f.ld_in = f.P;
     f.ld_out = f.P;
     f.tiles = (f.P + arrms::kFlatTile - 1) / arrms::kFlatTile;
-    f.nt_store = 1;
     (void)hipGetLastError();
     return launch_flat(dt, f, R, stream) == hipSuccess ? ARRMS_OK : ARRMS_ERR_HIP;
 }

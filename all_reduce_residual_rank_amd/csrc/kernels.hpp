@@ -222,7 +222,6 @@ ARRMS_DEV double wave_max_f64(double v)
 // not for its outstanding global loads and stores.
 ARRMS_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-ARRMS_DEV void st16(void *p, long long i, u32x4 v) { ((u32x4 *)p)[i] = v; }
 // Streaming (read-once / write-once) data: non-temporal accesses, so the rank
 // inputs and the outputs do not displace the reused lines (weights) in the
 // caches.
@@ -766,7 +765,7 @@ __global__ void __launch_bounds__(PPT == 1 ? 1024 : 512) row_kernel(const RowArg
 // bounds, and every thread still runs the same code path (PR #5807 Proposed
 // modifications: complete tiles unpredicated, leftover packs reduced by their
 // owner threads).
-template <int DT, int R, bool NTS>
+template <int DT, int R>
 ARRMS_DEV void flat_packs(const FlatArgs &a, long long src_row, long long dst_row,
                           const long long (&j)[kFlatPacksPerThread], const bool (&ok)[kFlatPacksPerThread])
 {
@@ -816,14 +815,11 @@ ARRMS_DEV void flat_packs(const FlatArgs &a, long long src_row, long long dst_ro
     for (int k = 0; k < NP; ++k) {
         if (!ok[k])
             continue;
-        if constexpr (NTS)
-            st16_nt(a.dst, dst_row + j[k], out[k]);
-        else
-            st16(a.dst, dst_row + j[k], out[k]);
+        st16_nt(a.dst, dst_row + j[k], out[k]);
     }
 }
 
-template <int DT, int R, bool TAIL, bool NTS>
+template <int DT, int R, bool TAIL>
 __global__ void __launch_bounds__(kFlatThreads) flat_kernel(const FlatArgs a)
 {
     const long long b = blockIdx.x;
@@ -838,7 +834,7 @@ __global__ void __launch_bounds__(kFlatThreads) flat_kernel(const FlatArgs a)
         j[k] = base + (long long)k * kFlatThreads;
         ok[k] = !last || j[k] < a.P;
     }
-    flat_packs<DT, R, NTS>(a, row * a.ld_in, row * a.ld_out, j, ok);
+    flat_packs<DT, R>(a, row * a.ld_in, row * a.ld_out, j, ok);
 }
 
 // --------------------------------------------------------------------------
@@ -947,17 +943,10 @@ static hipError_t flat_go(const FlatArgs &a, hipStream_t st)
         return hipErrorInvalidValue;
     const bool tail = a.P % kFlatTile != 0;
     dim3 grid((unsigned)blocks), block(kFlatThreads);
-    if (a.nt_store) {
-        if (tail)
-            hipLaunchKernelGGL((flat_kernel<DT, R, true, true>), grid, block, 0, st, a);
-        else
-            hipLaunchKernelGGL((flat_kernel<DT, R, false, true>), grid, block, 0, st, a);
-    } else {
-        if (tail)
-            hipLaunchKernelGGL((flat_kernel<DT, R, true, false>), grid, block, 0, st, a);
-        else
-            hipLaunchKernelGGL((flat_kernel<DT, R, false, false>), grid, block, 0, st, a);
-    }
+    if (tail)
+        hipLaunchKernelGGL((flat_kernel<DT, R, true>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((flat_kernel<DT, R, false>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 

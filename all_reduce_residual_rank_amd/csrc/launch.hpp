@@ -51,7 +51,6 @@ struct FlatArgs {
     long long ld_in;      // row stride of the inputs, in packs
     long long ld_out;     // row stride of dst, in packs
     long long tiles;      // tiles per row (ceil(P / kFlatTile))
-    int nt_store;         // non-temporal stores (the result is not read back soon)
 };
 
 // Row kernel shape: PPT packs per thread per row, tpr threads per row,
