@@ -73,6 +73,8 @@ template <> struct Fmt<DT_BF16> {
     // fp32 value exactly halfway between two bf16 values (bf16 drops 16 bits,
     // in the normal and the subnormal range alike)
     ARRMS_DEV bool tie_risk(float f) { return (__float_as_uint(f) & 0xffffu) == 0x8000u; }
+    // the lanes of the wave whose f is at risk, as a mask
+    ARRMS_DEV uint64_t tie_mask(float f) { return __builtin_amdgcn_ballot_w64(tie_risk(f)); }
     ARRMS_DEV float exact(double v) { return f64_to_f32_odd(v); }
 };
 
@@ -95,6 +97,13 @@ template <> struct Fmt<DT_FP16> {
     {
         return ((__float_as_uint(f) << 19) == 0x80000000u) | (__builtin_fabsf(f) < 0x1p-14f);
     }
+    // as a wave mask, one ballot per compare (each is then the compare's own
+    // lane mask; a ballot of the OR would go through a register)
+    ARRMS_DEV uint64_t tie_mask(float f)
+    {
+        return __builtin_amdgcn_ballot_w64((__float_as_uint(f) << 19) == 0x80000000u) |
+               __builtin_amdgcn_ballot_w64(__builtin_fabsf(f) < 0x1p-14f);
+    }
     ARRMS_DEV float exact(double v) { return f64_to_f32_odd(v); }
 };
 
@@ -103,6 +112,7 @@ template <> struct Fmt<DT_FP32> {
     ARRMS_DEV void unpack(uint32_t w, float (&f)[1]) { f[0] = __uint_as_float(w); }
     ARRMS_DEV uint32_t pack(const float (&f)[1]) { return __float_as_uint(f[0]); }
     ARRMS_DEV bool tie_risk(float) { return false; }
+    ARRMS_DEV uint64_t tie_mask(float) { return 0; }
     ARRMS_DEV float exact(double v) { return (float)v; }  // one RNE fp64 -> fp32
 };
 
@@ -400,31 +410,47 @@ ARRMS_DEV void reduce_pack(const u32x4 (&x)[R + 1], const u32x4 &w, double gadd,
 // range [2^-6, 464) and at least 4 fp32 ulps from an E4M3 tie: the 20 bits
 // below E4M3's mantissa, moved to the top of a word and offset, land at or
 // below 6 << 12 exactly when they are within 3 ulps of the halfway pattern
-// 0x80000. Elements that fail the test (rare) are recomputed alone by IEEE
-// division and the exact encoder; fast == false takes that path for all.
+// 0x80000. fast == true promises a normal, finite scale = fl32(amax / 448)
+// with amax >= |y| (the maximum of these very T values, as both callers
+// compute it); then |y * (1/scale)| <= 448 (1 + 2^-22) < 464, so only the
+// lower bound needs a test (a NaN fails it too). Elements that fail the test
+// (rare) are recomputed alone by IEEE division and the exact encoder; fast ==
+// false takes that path for all.
+ARRMS_DEV bool e4m3_fast_bad(float cq)
+{
+    const uint32_t t = (__float_as_uint(cq) << 12) + 0x80003000u;
+    return !(__builtin_fabsf(cq) >= 0x1p-6f) | (t <= 0x6000u);
+}
+
 ARRMS_DEV u32x2 quant8_e4m3(const float (&y)[8], float scale, float inv, bool fast)
 {
     u32x2 q = {0u, 0u};
     if (fast) {
         float cq[8];
-        bool bad[8];
         uint64_t anybad = 0;  // wave mask
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
+            // the two halves of e4m3_fast_bad as separate ballots: each is then
+            // the compare's own lane mask (a ballot of their OR would first
+            // turn the mask into a register and back)
             cq[e] = y[e] * inv;
-            const float m = __builtin_fabsf(cq[e]);
             const uint32_t t = (__float_as_uint(cq[e]) << 12) + 0x80003000u;
-            bad[e] = !(m >= 0x1p-6f) | !(m < 464.0f) | (t <= 0x6000u);
-            anybad |= __builtin_amdgcn_ballot_w64(bad[e]);
+            anybad |= __builtin_amdgcn_ballot_w64(!(__builtin_fabsf(cq[e]) >= 0x1p-6f));
+            anybad |= __builtin_amdgcn_ballot_w64(t <= 0x6000u);
         }
         q.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[0], cq[1], 0, false);
         q.x = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[2], cq[3], (int)q.x, true);
         q.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[4], cq[5], 0, false);
         q.y = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cq[6], cq[7], (int)q.y, true);
         if (anybad != 0) {
+            // the test again, on opaque copies: keeping its results from above
+            // alive would cost registers and instructions on the common path
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                if (__builtin_amdgcn_ballot_w64(bad[e]) != 0 && bad[e]) {
+                float c = cq[e];
+                asm volatile("" : "+v"(c));
+                const bool bad = e4m3_fast_bad(c);
+                if (__builtin_amdgcn_ballot_w64(bad) != 0 && bad) {
                     const uint32_t b = e4m3_encode(y[e] / scale);
                     const int sh = 8 * (e & 3);
                     if (e < 4)
@@ -661,7 +687,7 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
 #pragma unroll
                     for (int e = 0; e < EPW; ++e) {
                         yf[e] = (float)((double)(hf[e] * wf[e]) * rstd);
-                        risk |= __builtin_amdgcn_ballot_w64(F::tie_risk(yf[e]));
+                        risk |= F::tie_mask(yf[e]);
                     }
                     yv[i] = F::pack(yf);
                 }
@@ -675,7 +701,7 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
                     for (int e = 0; e < EPW; ++e) {
                         const double we = (double)wf[e] + gadd;
                         yf[e] = (float)(((double)hf[e] * we) * rstd);
-                        risk |= __builtin_amdgcn_ballot_w64(F::tie_risk(yf[e]));
+                        risk |= F::tie_mask(yf[e]);
                     }
                     yv[i] = F::pack(yf);
                 }
