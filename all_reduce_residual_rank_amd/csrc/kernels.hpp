@@ -33,6 +33,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 #define ARRMS_DEV static __device__ __forceinline__
 
@@ -70,11 +71,10 @@ template <> struct Fmt<DT_BF16> {
         f32x2 v = {f[0], f[1]};
         return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
     }
-    // fp32 value exactly halfway between two bf16 values (bf16 drops 16 bits,
-    // in the normal and the subnormal range alike)
-    ARRMS_DEV bool tie_risk(float f) { return (__float_as_uint(f) & 0xffffu) == 0x8000u; }
-    // the lanes of the wave whose f is at risk, as a mask
-    ARRMS_DEV uint64_t tie_mask(float f) { return __builtin_amdgcn_ballot_w64(tie_risk(f)); }
+    // the lanes of the wave whose fp32 value f sits exactly halfway between
+    // two bf16 values (bf16 drops 16 bits, in the normal and the subnormal
+    // range alike), as a mask
+    ARRMS_DEV uint64_t tie_mask(float f) { return __builtin_amdgcn_ballot_w64((__float_as_uint(f) & 0xffffu) == 0x8000u); }
     ARRMS_DEV float exact(double v) { return f64_to_f32_odd(v); }
 };
 
@@ -91,14 +91,10 @@ template <> struct Fmt<DT_FP16> {
         f32x2 v = {f[0], f[1]};
         return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
     }
-    // a tie of the normal fp16 range (13 dropped bits, incl. 65520 -> inf),
-    // or anything below 2^-14 (fp16 subnormals drop more bits): exact branch
-    ARRMS_DEV bool tie_risk(float f)
-    {
-        return ((__float_as_uint(f) << 19) == 0x80000000u) | (__builtin_fabsf(f) < 0x1p-14f);
-    }
-    // as a wave mask, one ballot per compare (each is then the compare's own
-    // lane mask; a ballot of the OR would go through a register)
+    // lanes at risk, as a wave mask: a tie of the normal fp16 range (13
+    // dropped bits, incl. 65520 -> inf), or anything below 2^-14 (fp16
+    // subnormals drop more bits). One ballot per compare: each is then the
+    // compare's own lane mask (a ballot of the OR would go through a register)
     ARRMS_DEV uint64_t tie_mask(float f)
     {
         return __builtin_amdgcn_ballot_w64((__float_as_uint(f) << 19) == 0x80000000u) |
@@ -111,24 +107,9 @@ template <> struct Fmt<DT_FP32> {
     static constexpr int EPW = 1;
     ARRMS_DEV void unpack(uint32_t w, float (&f)[1]) { f[0] = __uint_as_float(w); }
     ARRMS_DEV uint32_t pack(const float (&f)[1]) { return __float_as_uint(f[0]); }
-    ARRMS_DEV bool tie_risk(float) { return false; }
     ARRMS_DEV uint64_t tie_mask(float) { return 0; }
     ARRMS_DEV float exact(double v) { return (float)v; }  // one RNE fp64 -> fp32
 };
-
-// RNE_T of one fp64 value, returned as its (exact) fp32 value.
-template <int DT> ARRMS_DEV float round_one(double v, bool exact_only)
-{
-    using F = Fmt<DT>;
-    float f = (float)v;
-    if (exact_only || F::tie_risk(f))
-        f = F::exact(v);
-    float r[F::EPW] = {};
-    float in[F::EPW] = {};
-    in[0] = f;
-    F::unpack(F::pack(in), r);
-    return r[0];
-}
 
 // --------------------------------------------------------------------------
 // FP8 E4M3 ("fn": bias 7, max 448, no infinities, S.1111.111 = NaN).
@@ -199,13 +180,6 @@ template <bool ROW32> ARRMS_DEV double sum_across(double v)
     return a + b;
 }
 
-template <bool ROW32> ARRMS_DEV double max_across(double v)
-{
-    double a, b;
-    pair_f64<ROW32>(v, a, b);
-    return __builtin_fmax(a, b);
-}
-
 ARRMS_DEV double wave_sum_f64(double v)
 {
     v += dpp_f64<0xB1>(v);   // quad_perm [1,0,3,2]
@@ -214,17 +188,6 @@ ARRMS_DEV double wave_sum_f64(double v)
     v += dpp_f64<0x140>(v);  // row_mirror
     v = sum_across<false>(v);  // rows 0+1, 2+3
     v = sum_across<true>(v);   // halves
-    return v;
-}
-
-ARRMS_DEV double wave_max_f64(double v)
-{
-    v = __builtin_fmax(v, dpp_f64<0xB1>(v));
-    v = __builtin_fmax(v, dpp_f64<0x4E>(v));
-    v = __builtin_fmax(v, dpp_f64<0x141>(v));
-    v = __builtin_fmax(v, dpp_f64<0x140>(v));
-    v = max_across<false>(v);
-    v = max_across<true>(v);
     return v;
 }
 
@@ -359,11 +322,9 @@ ARRMS_DEV __amdgpu_buffer_rsrc_t out_stream(const void *base, long long row, lon
 }
 
 // Phase-1 arithmetic of one pack: rank sum in fp32, RNE to T, residual add,
-// RNE to T (h), exact squares of h into fp64 partial sums, and for FP8 the
-// running max of |h * w_eff|.
-template <int DT, int R, bool FP8>
-ARRMS_DEV void reduce_pack(const u32x4 (&x)[R + 1], const u32x4 &w, double gadd, u32x4 &hv,
-                           double (&ssw)[4], double &pm)
+// RNE to T (h), exact squares of h into fp64 partial sums.
+template <int DT, int R>
+ARRMS_DEV void reduce_pack(const u32x4 (&x)[R + 1], u32x4 &hv, double (&ssw)[4])
 {
     using F = Fmt<DT>;
     constexpr int EPW = F::EPW;
@@ -392,15 +353,6 @@ ARRMS_DEV void reduce_pack(const u32x4 (&x)[R + 1], const u32x4 &w, double gadd,
         for (int e = 0; e < EPW; ++e) {
             const double hd = (double)hf[e];
             ssw[i] = __builtin_fma(hd, hd, ssw[i]);  // h^2 is exact in fp64
-        }
-        if constexpr (FP8) {
-            float wf[EPW];
-            F::unpack(w[i], wf);
-#pragma unroll
-            for (int e = 0; e < EPW; ++e) {
-                const double we = (double)wf[e] + gadd;
-                pm = __builtin_fmax(pm, __builtin_fabs((double)hf[e] * we));
-            }
         }
     }
 }
@@ -501,6 +453,16 @@ template <int N> ARRMS_DEV uint32_t group_max_u32(uint32_t v)
     return v;
 }
 
+// max over the whole wave: 16-lane rows by DPP, then across rows
+ARRMS_DEV uint32_t wave_max_u32(uint32_t v)
+{
+    v = group_max_u32<16>(v);
+    u32x2 t = swap_pair<false>(v);
+    v = t.x > t.y ? t.x : t.y;
+    t = swap_pair<true>(v);
+    return t.x > t.y ? t.x : t.y;
+}
+
 // E8M0 code of an MX block scale from the block's max |y| bits (OCP
 // Microscaling Formats v1.0, section 6.3): 2^(floor(log2 amax) - 2) for E2M1,
 // the exponent clamped at -127 (zero and tiny blocks: code 0); a NaN or an
@@ -539,7 +501,8 @@ ARRMS_DEV uint32_t mx_pack8(const float (&y)[8], uint32_t code)
 // The rows of one block: row group g = blockIdx.x, then g + gridDim.x, ...
 // (with the default grid of one block per row group the loop runs once).
 template <int DT, int R, int PPT, int EPI, int WIN>
-ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMaxWavesPerBlock][2])
+ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMaxWavesPerBlock],
+                        uint32_t (&redm)[kMaxWavesPerBlock])
 {
     using F = Fmt<DT>;
     constexpr int EPW = F::EPW;
@@ -560,12 +523,11 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
 
     for (long long g = blockIdx.x; g < a.groups; g += gridDim.x) {
         // The weights (the same columns for every row, from L2) are read per
-        // row: with FP8 before the row's inputs (the row maximum needs them in
-        // phase 1), otherwise once the inputs are all issued, so that they
-        // neither hold registers through phase 1 nor sit in the load window.
+        // row, once the inputs are all issued, so that they neither hold
+        // registers through phase 1 nor sit in the load window.
         const __amdgpu_buffer_rsrc_t rw = row_rsrc(a.weight, 0, 0, rb);
         u32x4 w[PPT];
-        if constexpr (FP8 || !ARRMS_LATE_WEIGHTS) {
+        if constexpr (!ARRMS_LATE_WEIGHTS) {
 #pragma unroll
             for (int k = 0; k < PPT; ++k)
                 w[k] = bload_cached(rw, (uint32_t)(c.lt + k * c.tpr) * 16u);
@@ -574,14 +536,13 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
         __amdgpu_buffer_rsrc_t sin[NS];
         in_streams<R>(a, row, rb, sin);
 
-        // ---- rank sum, residual add, sum of squares (and max |h * w_eff|):
+        // ---- rank sum, residual add, sum of squares:
         // load i is stream i % NS of pack i / NS; after issuing load i the
         // window waits for load i - (W - 1), and a pack is reduced as soon
         // as its last stream has landed
         u32x4 x[PPT][NS];
         u32x4 hv[PPT];
         double ssw[4] = {0.0, 0.0, 0.0, 0.0};  // one partial sum of squares per word
-        double pm = 0.0;
         // steps i = 0 .. NL + W - 2, as (kk, r) with i = kk * NS + r
         constexpr int KK = (NL + W - 1 + NS - 1) / NS;
 #pragma unroll
@@ -595,7 +556,7 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
                     x[kk][r] = bload(sin[r], (uint32_t)(c.lt + kk * c.tpr) * 16u);  // kk < PPT here
                     wait_vm<W - 1>();
                 }
-                if constexpr (!FP8 && ARRMS_LATE_WEIGHTS) {
+                if constexpr (ARRMS_LATE_WEIGHTS) {
                     if (i == NL - 1) {
 #pragma unroll
                         for (int k = 0; k < PPT; ++k)
@@ -605,7 +566,7 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
                 const int j = i - (W - 1);
                 if (j >= 0 && j % NS == NS - 1) {
                     const int k = j / NS;
-                    reduce_pack<DT, R, FP8>(x[k], w[k], gadd, hv[k], ssw, pm);
+                    reduce_pack<DT, R>(x[k], hv[k], ssw);
                     if constexpr (W == NL && !ARRMS_ROUT_LATE_ALL)
                         bstore(hv[k], out_stream(a.residual_out, row, a.ld_rout, rb, a.M),
                                (uint32_t)(c.lt + k * c.tpr) * 16u);
@@ -616,22 +577,14 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
         // ---- row reduction: wave DPP tree, then the row group's waves via LDS
         double ss = (ssw[0] + ssw[1]) + (ssw[2] + ssw[3]);
         ss = wave_sum_f64(ss);
-        if constexpr (FP8)
-            pm = wave_max_f64(pm);
         if (c.wpr > 1) {
-            if (c.lane == 0) {
-                red[parity][c.wave][0] = ss;
-                red[parity][c.wave][1] = pm;
-            }
+            if (c.lane == 0)
+                red[parity][c.wave] = ss;
             lds_barrier();
             const int w0 = c.slot * c.wpr;
-            ss = red[parity][w0][0];
-            pm = red[parity][w0][1];
-            for (int w = 1; w < c.wpr; ++w) {
-                ss += red[parity][w0 + w][0];
-                if constexpr (FP8)
-                    pm = __builtin_fmax(pm, red[parity][w0 + w][1]);
-            }
+            ss = red[parity][w0];
+            for (int w = 1; w < c.wpr; ++w)
+                ss += red[parity][w0 + w];
             parity ^= 1;
         }
 
@@ -657,17 +610,12 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
                 bstore(hv[k], rout, (uint32_t)(c.lt + k * c.tpr) * 16u);
         }
         const double rstd = 1.0 / __builtin_sqrt(ss / (double)a.H + (double)a.eps);
-        float scale = 0.0f, inv = 0.0f;
-        bool qfast = false;
-        if constexpr (FP8) {
-            // max |y| = RNE_T(max |h * w_eff| * rstd): rounding is monotone
-            const float amax = round_one<DT>(pm * rstd, exact_only);
-            scale = amax / 448.0f;
-            inv = 1.0f / scale;
-            qfast = !exact_only && scale >= 1.17549435e-38f && scale <= 3.0e38f;
-            if (c.lt == 0 && row < a.M)
-                a.fp8_scale[row] = scale;
-        }
+        // per-token FP8: the T-rounded y of every pack is kept for the quant,
+        // which needs the row's max |y|; the maximum is taken on the T bits
+        // with the sign cleared (their integer order is the order of |y|, and
+        // a NaN ranks above infinity), two 16-bit lanes per word
+        u32x4 yk[FP8 ? PPT : 1];
+        u16x2 ym = {0, 0};
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
             const uint32_t off = (uint32_t)(c.lt + k * c.tpr) * 16u;
@@ -725,7 +673,13 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
             if constexpr (GROUPQ)
                 if (a.out)
                     bstore(yv, rout_t, off);
-            if constexpr ((FP8 || GROUPQ) && DT != DT_FP32) {
+            if constexpr (FP8 && DT != DT_FP32) {
+                yk[k] = yv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    ym = __builtin_elementwise_max(ym, __builtin_bit_cast(u16x2, yv[i] & 0x7fff7fffu));
+            }
+            if constexpr (GROUPQ && DT != DT_FP32) {
                 float y[8];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -735,9 +689,7 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
                     y[2 * i + 1] = t[1];
                 }
                 const int pack = c.lt + k * c.tpr;  // pack index in the row
-                if constexpr (FP8) {
-                    bstore8(quant8_e4m3(y, scale, inv, qfast), rout_q, off / 2u);
-                } else if constexpr (EPI == EPI_FP8G) {
+                if constexpr (EPI == EPI_FP8G) {
                     // group max over the 16 lanes holding a group's 16 packs
                     const float gmax = __uint_as_float(group_max_u32<16>(absmax_bits(y)));
                     const float gscale = gmax / 448.0f;
@@ -753,6 +705,39 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
                     if ((pack & 3) == 0 && pack < c.P && row < a.M)
                         ((uint8_t *)a.q_scale)[row * a.qgroups + (pack >> 2)] = (uint8_t)code;
                 }
+            }
+        }
+        if constexpr (FP8 && DT != DT_FP32) {
+            // the row's max |y|: wave tree, then the row group's waves via LDS
+            // (a second barrier; the row's waves have all read red by then)
+            uint32_t am = wave_max_u32(ym.x > ym.y ? ym.x : ym.y);
+            if (c.wpr > 1) {
+                if (c.lane == 0)
+                    redm[c.wave] = am;
+                lds_barrier();
+                const int w0 = c.slot * c.wpr;
+                am = redm[w0];
+                for (int w = 1; w < c.wpr; ++w)
+                    am = redm[w0 + w] > am ? redm[w0 + w] : am;
+            }
+            float amx[EPW];
+            F::unpack(am, amx);  // the T value in the low half
+            const float scale = amx[0] / 448.0f;
+            const float inv = 1.0f / scale;
+            const bool qfast = !exact_only && scale >= 1.17549435e-38f && scale <= 3.0e38f;
+            if (c.lt == 0 && row < a.M)
+                a.fp8_scale[row] = scale;
+#pragma unroll
+            for (int k = 0; k < PPT; ++k) {
+                float y[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float t[2];
+                    F::unpack(yk[k][i], t);
+                    y[2 * i] = t[0];
+                    y[2 * i + 1] = t[1];
+                }
+                bstore8(quant8_e4m3(y, scale, inv, qfast), rout_q, (uint32_t)(c.lt + k * c.tpr) * 8u);
             }
         }
     }
@@ -776,9 +761,10 @@ __global__ void __launch_bounds__(PPT == 1 ? 1024 : 512) row_kernel(const RowArg
     c.lane = tid & 63;
     c.P = a.P;
 
-    __shared__ double red[2][kMaxWavesPerBlock][2];
+    __shared__ double red[2][kMaxWavesPerBlock];
+    __shared__ uint32_t redm[kMaxWavesPerBlock];
 
-    row_loop<DT, R, PPT, EPI, WIN>(a, c, red);
+    row_loop<DT, R, PPT, EPI, WIN>(a, c, red, redm);
 }
 
 // --------------------------------------------------------------------------
