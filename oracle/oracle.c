@@ -42,6 +42,13 @@
  * For T = fp32 the RNE_T steps of O1/O2 are the fp32 operations
  * themselves and O4 rounds fp64 -> fp32 once.
  *
+ * Non-finite values (the pages define none; read here as IEEE arithmetic
+ * plus three rules): a maximum over |y| is NaN when any y it covers is NaN
+ * (max_abs_nan below); the E4M3 code of any NaN is 0x7F, with no sign (a
+ * NaN's sign is not fixed by the arithmetic that made it); in an MXFP4
+ * block whose scale is the NaN code a NaN element is 0x7, other elements
+ * +-6's code with the sign of y.
+ *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math -fPIC -shared.
  * -ffp-contract=off keeps every fp32/fp64 operation a separate IEEE
  * operation, as written.
@@ -157,9 +164,9 @@ double orc_fp16_to_double(uint16_t h)
  * +-448. */
 uint8_t orc_e4m3_from_float(float x)
 {
-    uint8_t sign = signbit(x) ? 0x80u : 0;
     if (isnan(x))
-        return (uint8_t)(sign | 0x7Fu);
+        return 0x7Fu; /* one NaN code, no sign */
+    uint8_t sign = signbit(x) ? 0x80u : 0;
     double r = fabs(round_p((double)x, 4, -6));
     if (isinf(x) || r > 448.0)
         r = 448.0;
@@ -172,6 +179,14 @@ uint8_t orc_e4m3_from_float(float x)
     int lead = e - 1;
     uint8_t mant = (uint8_t)(ldexp(f, 4) - 8.0); /* 3 fraction bits */
     return (uint8_t)(sign | (uint8_t)((lead + 7) << 3) | mant);
+}
+
+/* Running max of |y| that a NaN takes over and keeps. */
+static float max_abs_nan(float amax, float y)
+{
+    if (isnan(amax) || isnan(y))
+        return NAN;
+    return fabsf(y) > amax ? fabsf(y) : amax;
 }
 
 /* OCP FP4 E2M1 (the MX element format): 2 significant bits, emin = 0
@@ -341,8 +356,7 @@ int oracle_fused_rows(const void *const *rank_in, int R, const void *residual,
             h_scratch[j] = y; /* h is no longer needed */
             if (out)
                 store_t(out, row + j, y, dt);
-            if (fabsf(y) > amax)
-                amax = fabsf(y);
+            amax = max_abs_nan(amax, y);
         }
 
         /* O5: dynamic per-token FP8 of the T-rounded output */
@@ -367,8 +381,7 @@ int oracle_fused_rows(const void *const *rank_in, int R, const void *residual,
                 const float *yg = h_scratch + (size_t)g * ORC_FP8_GROUP;
                 float gmax = 0.0f;
                 for (int j = 0; j < ORC_FP8_GROUP; ++j)
-                    if (fabsf(yg[j]) > gmax)
-                        gmax = fabsf(yg[j]);
+                    gmax = max_abs_nan(gmax, yg[j]);
                 float scale = gmax / 448.0f;
                 ((float *)fp8_scale)[(size_t)m * ng + g] = scale;
                 for (int j = 0; j < ORC_FP8_GROUP; ++j) {
@@ -400,7 +413,9 @@ int oracle_fused_rows(const void *const *rank_in, int R, const void *residual,
                     uint8_t c[2];
                     for (int t = 0; t < 2; ++t) {
                         float y = yb[j + t];
-                        if (code == 0xFFu)
+                        if (code == 0xFFu && isnan(y))
+                            c[t] = 0x7u;
+                        else if (code == 0xFFu)
                             c[t] = (uint8_t)((signbit(y) ? 0x8u : 0) | 0x7u);
                         else
                             c[t] = orc_e2m1_from_float((float)ldexp((double)y, 127 - (int)code));
@@ -443,8 +458,7 @@ int oracle_quant_rows(const void *y_in, int dt, int M, int H, uint8_t *q_out,
         float amax = 0.0f;
         for (int j = 0; j < H; ++j) {
             float y = load_t(y_in, row + j, dt);
-            if (fabsf(y) > amax)
-                amax = fabsf(y);
+            amax = max_abs_nan(amax, y);
         }
         float scale = amax / 448.0f;
         scale_out[m] = scale;
