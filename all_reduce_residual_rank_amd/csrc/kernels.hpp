@@ -113,14 +113,16 @@ template <> struct Fmt<DT_FP32> {
 
 // --------------------------------------------------------------------------
 // FP8 E4M3 ("fn": bias 7, max 448, no infinities, S.1111.111 = NaN).
-// Exact encoder written from the format: RNE, saturating to +-448.
+// Exact encoder written from the format: RNE, saturating to +-448. Every NaN
+// gets the one code 0x7F: the sign of a NaN is not fixed by the arithmetic
+// that produced it.
 ARRMS_DEV uint32_t e4m3_encode(float x)
 {
     uint32_t b = __float_as_uint(x);
     uint32_t s = (b >> 24) & 0x80u;
     float a = __builtin_fabsf(x);
     if (!(a == a))
-        return s | 0x7fu;
+        return 0x7fu;
     if (a >= 464.0f)  // midpoint of 448 and (unrepresentable) 480 and beyond
         return s | 0x7eu;
     if (a < 0.015625f) {  // below 2^-6: multiples of 2^-9 (code 8 = 2^-6)
@@ -479,21 +481,38 @@ ARRMS_DEV uint32_t mx_scale_code(uint32_t am)
 // two), then round to nearest, ties to even, saturating at 6 -- counted as the
 // number of E2M1 decision points the magnitude passes (a tie goes up only when
 // the upper neighbour's code is even); packed two per byte, the even column in
-// the low nibble. A block with a NaN or an infinity gets +-6's code throughout.
+// the low nibble. A block with a NaN or an infinity (scale code 0xFF) gets
+// +-6's code throughout with the sign of y, and 0x7 for a NaN element (its
+// sign is not fixed by the arithmetic); such blocks take a separate,
+// wave-uniform branch.
 ARRMS_DEV uint32_t mx_pack8(const float (&y)[8], uint32_t code)
 {
     const float f = __uint_as_float((254u - (code < 254u ? code : 253u)) << 23);  // 2^(127 - code)
     uint32_t word = 0;
+    if (__builtin_amdgcn_ballot_w64(code == 0xffu) == 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float a = __builtin_fabsf(y[e] * f);
-        uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                     (uint32_t)(a > 5.0f);
-        if (code == 0xffu)
-            c = 7u;
-        c |= (__float_as_uint(y[e]) >> 28) & 0x8u;
-        word |= c << (4 * e);
+        for (int e = 0; e < 8; ++e) {
+            const float a = __builtin_fabsf(y[e] * f);
+            uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                         (uint32_t)(a > 5.0f);
+            c |= (__float_as_uint(y[e]) >> 28) & 0x8u;
+            word |= c << (4 * e);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float a = __builtin_fabsf(y[e] * f);
+            uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                         (uint32_t)(a > 5.0f);
+            const uint32_t sg = (__float_as_uint(y[e]) >> 28) & 0x8u;
+            if (code == 0xffu)
+                c = y[e] == y[e] ? (7u | sg) : 7u;
+            else
+                c |= sg;
+            word |= c << (4 * e);
+        }
     }
     return word;
 }
