@@ -83,7 +83,9 @@ extern "C" {
  *                                                    one rounding from fp64 -> out[m][j]
  *   FP8:   amax = max_j |y| ; scale = fl32(amax / 448) -> fp8_scale[m]
  *          q = E4M3_RNE_saturating( fl32(y / scale) ) -> fp8_out[m][j]
- *          (amax == 0 gives scale 0 and q = +-0 with the sign of y)
+ *          (amax == 0 gives scale 0 and q = +-0 with the sign of y; a NaN y
+ *          makes amax and the scale NaN, and every NaN quotient codes as
+ *          0x7F, without sign)
  * For T = fp32 the two RNE_T steps before the norm are the fp32 operations.
  *
  * rank_in      host array of R device pointers, each to [M][H] T (row-major,
@@ -151,13 +153,15 @@ ARRMS_API int arrms_fused_strided(const void *const *rank_in, int R, const void 
  *   ARRMS_QUANT_FP8_GROUP  the per-token FP8 steps on each group of
  *       ARRMS_FP8_GROUP_SIZE (128) consecutive columns: scale = fl32(gmax /
  *       448) over the T-rounded y of the group, q = E4M3_RNE_sat(fl32(y /
- *       scale)), an all-zero group gives scale 0 and signed zeros.
+ *       scale)), an all-zero group gives scale 0 and signed zeros, a NaN
+ *       in the group a NaN scale and codes 0x7F.
  *       q_out: [M][H] E4M3 codes; q_scale: [M][H/128] fp32 (4-byte aligned).
  *   ARRMS_QUANT_MXFP4  OCP Microscaling Formats v1.0 MXFP4 over blocks of
  *       ARRMS_MX_BLOCK (32) columns: X = 2^(floor(log2 bmax) - 2) with the
  *       exponent clamped to [-127, 127], stored as its E8M0 code (an all-zero
  *       block gives code 0; a NaN or an infinity in the block gives 0xFF and
- *       +-6's element code); elements E2M1_RNE_sat(y / X) (y / X is exact).
+ *       +-6's element code with y's sign, 0x7 for a NaN element); elements
+ *       E2M1_RNE_sat(y / X) (y / X is exact).
  *       q_out: [M][H/2] bytes, two codes per byte, the even column in the
  *       low nibble (sign in bit 3 of each nibble); q_scale: [M][H/32] bytes.
  *   ARRMS_QUANT_FP8_TOKEN  exactly arrms_fused with ARRMS_FP8 (q_scale [M] fp32).
