@@ -144,3 +144,49 @@ def test_token_quant_equals_arrms_fused_fp8():
     assert np.array_equal(gu.host_bits(q), a["fp8"])
     assert np.array_equal(gu.host_bits(sc), a["scale"])
     assert np.array_equal(gu.host_bits(out), a["out"])
+
+
+@pytest.mark.parametrize("quant", [2, 3], ids=["fp8group", "mxfp4"])
+def test_group_quant_graph_replay(quant):
+    # one captured call per path, replayed with new inputs copied into the
+    # captured buffers and poisoned outputs, each replay against the oracle
+    dev = torch.device("cuda")
+    wl = wlmod.Workload("q_graph", R=3, M=200, H=2048, dtype="fp16", gemma=True, w_mean=0.0)
+    arrms.arrms_reserve_staging(0)
+    xs0, res0, w0 = wlmod.make_inputs(wl, seed=0)
+    xd = [x.to(dev) for x in xs0]
+    rd, wd = res0.to(dev), w0.to(dev)
+    qshape, _, sshape, sdt = _shapes(quant, wl.M, wl.H)
+    bufs, graphs = {}, {}
+    for path in ("one", "two"):
+        b = {"out": torch.empty(wl.M, wl.H, dtype=torch.float16, device=dev),
+             "rout": torch.empty(wl.M, wl.H, dtype=torch.float16, device=dev),
+             "q": torch.empty(qshape, dtype=torch.uint8, device=dev),
+             "sc": torch.empty(sshape, dtype=sdt, device=dev)}
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            arrms.arrms_fused_quant(xd, rd, wd, b["out"], b["rout"], b["q"], b["sc"], eps=wl.eps,
+                                    flags=wl.flags | PATHS[path], quant=quant, stream=s)
+        torch.cuda.current_stream().wait_stream(s)
+        bufs[path], graphs[path] = b, g
+    for step in range(3):
+        xs, res, w = wlmod.make_inputs(wl, seed=20 + step)
+        for d, h in zip(xd, xs):
+            d.copy_(h)
+        rd.copy_(res)
+        wd.copy_(w)
+        want = _oracle(wl, xs, res, w, quant, True)
+        for path in ("one", "two"):
+            b = bufs[path]
+            for t in b.values():
+                gu.poison_(t)
+            torch.cuda.synchronize()
+            print(f"group-quant graph replay quant={quant} path={path} step={step}", flush=True)
+            graphs[path].replay()
+            torch.cuda.synchronize()
+            got = {"out": gu.host_bits(b["out"]), "residual_out": gu.host_bits(b["rout"]),
+                   "fp8": gu.host_bits(b["q"]),
+                   "scale": gu.host_bits(b["sc"]) if sdt == torch.uint8 else gu.host_bits(b["sc"])}
+            _check(got, want, f"graph/q{quant}/{path}/{step}")

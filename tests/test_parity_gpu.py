@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from all_reduce_residual_rank_amd import workloads as wlmod
 from tests import gpu_util as gu
 
@@ -327,3 +328,53 @@ def test_launch_shapes_match_oracle(wl, shape):
     print(f"case {wl.name} shape={shape}", flush=True)
     got = _run_config(wl, xs, res, w, wl.flags | PATHS["one"], ppt, tpr, rpb, blocks, window)
     gu.compare(got, want, wl.dtype, label=f"{wl.name}/{shape}")
+
+
+def test_concurrent_streams():
+    # one-stage calls keep no state between calls: calls of different shapes,
+    # dtypes and entry points enqueued on three streams at once must each give
+    # the oracle's bits
+    dev = torch.device("cuda")
+    wa = wlmod.Workload("conc_a", R=4, M=300, H=6144, row_scale=(0.1, 10.0))
+    wb = wlmod.Workload("conc_b", R=2, M=200, H=2880, dtype="fp16", gemma=True, fp8=True, mirror=True,
+                        w_mean=0.0)
+    ins = {}
+    for wl, seed in ((wa, 41), (wb, 42)):
+        xs, res, w = wlmod.make_inputs(wl, seed=seed)
+        ins[wl.name] = (xs, res, w, [x.to(dev) for x in xs], res.to(dev), w.to(dev))
+    sx = wlmod.make_sum_inputs(3, 1 << 20, 43, "bf16", sigma=1.0)
+    sxd = [x.to(dev) for x in sx]
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    print("concurrent streams: 2 x (bf16 300x6144, fp16 gemma FP8 200x2880, sum 1M)", flush=True)
+    for rep in range(2):
+        xs, res, w, xd, rd, wd = ins["conc_a"]
+        oa = gu.poison_(torch.empty(wa.M, wa.H, dtype=torch.bfloat16, device=dev))
+        ra = gu.poison_(torch.empty(wa.M, wa.H, dtype=torch.bfloat16, device=dev))
+        xs, res, w, xd2, rd2, wd2 = ins["conc_b"]
+        ob = gu.poison_(torch.empty(wb.M, wb.H, dtype=torch.float16, device=dev))
+        rb = gu.poison_(torch.empty(wb.M, wb.H, dtype=torch.float16, device=dev))
+        qb = gu.poison_(torch.empty(wb.M, wb.H, dtype=torch.uint8, device=dev))
+        sb = gu.poison_(torch.empty(wb.M, dtype=torch.float32, device=dev))
+        so = gu.poison_(torch.empty(1 << 20, dtype=torch.bfloat16, device=dev))
+        for s in streams:
+            s.wait_stream(torch.cuda.current_stream())
+        arrms.arrms_fused(xd, rd, wd, oa, ra, eps=wa.eps, flags=wa.flags | PATHS["one"], stream=streams[0])
+        arrms.arrms_fused(xd2, rd2, wd2, ob, rb, qb, sb, eps=wb.eps, flags=wb.flags | PATHS["one"],
+                          stream=streams[1])
+        arrms.arrms_allreduce_sum(sxd, so, flags=arrms.DTYPE_BF16, stream=streams[2])
+        outs.append((oa, ra, ob, rb, qb, sb, so))
+    torch.cuda.synchronize()
+    xs, res, w = ins["conc_a"][:3]
+    want_a = gu.run_oracle(wa, xs, res, w)
+    xs, res, w = ins["conc_b"][:3]
+    want_b = gu.run_oracle(wb, xs, res, w)
+    want_s = oracle.rank_sum([gu.host_bits(x) for x in sx], wlmod.DT_CODE["bf16"])
+    for rep, (oa, ra, ob, rb, qb, sb, so) in enumerate(outs):
+        gu.compare({"out": gu.host_bits(oa), "residual_out": gu.host_bits(ra), "fp8": None, "scale": None},
+                   want_a, "bf16", label=f"conc-a-{rep}")
+        gu.compare({"out": gu.host_bits(ob), "residual_out": gu.host_bits(rb), "fp8": gu.host_bits(qb),
+                    "scale": gu.host_bits(sb)}, want_b, "fp16", label=f"conc-b-{rep}")
+        assert np.array_equal(gu.host_bits(so), want_s), f"conc-sum-{rep}"

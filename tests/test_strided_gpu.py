@@ -158,3 +158,45 @@ def test_fp8_rows_eight_byte_aligned(path):
         want = gu.run_oracle(wl, xs, res, w)
         got = _run_strided(wl, xs, res, w, path, pads)
         gu.compare(got, want, wl.dtype, label=f"{wl.name}/{path}")
+
+
+def test_strided_graph_replay():
+    # arrms_fused_strided captured once per path and replayed with new inputs
+    wl = wlmod.Workload("s_graph", R=4, M=90, H=2880, row_scale=(0.1, 10.0))
+    arrms.arrms_reserve_staging(0)
+    dev = torch.device("cuda")
+    M, H = wl.M, wl.H
+    xs0, res0, w0 = wlmod.make_inputs(wl, seed=0)
+    xin = [_padded(M, H + 32, 16, H, torch.bfloat16, x.cuda())[1] for x in xs0]
+    _, rd = _padded(M, H + 8, 0, H, torch.bfloat16, res0.cuda())
+    wd = w0.to(dev)
+    bufs, graphs = {}, {}
+    for path in ("one", "two"):
+        ob, out = _padded(M, H + 64, 8, H, torch.bfloat16)
+        rb, rout = _padded(M, H + 8, 8, H, torch.bfloat16)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            arrms.arrms_fused_strided(xin, rd, wd, out, rout, eps=wl.eps, flags=wl.flags | PATHS[path],
+                                      stream=s)
+        torch.cuda.current_stream().wait_stream(s)
+        bufs[path], graphs[path] = (ob, out, rb, rout), g
+    for step in range(3):
+        xs, res, w = wlmod.make_inputs(wl, seed=30 + step)
+        for d, h in zip(xin, xs):
+            d.copy_(h)
+        rd.copy_(res)
+        wd.copy_(w)
+        want = gu.run_oracle(wl, xs, res, w)
+        for path in ("one", "two"):
+            ob, out, rb, rout = bufs[path]
+            gu.poison_(ob)
+            gu.poison_(rb)
+            torch.cuda.synchronize()
+            print(f"strided graph replay path={path} step={step}", flush=True)
+            graphs[path].replay()
+            torch.cuda.synchronize()
+            got = {"out": gu.host_bits(out), "residual_out": gu.host_bits(rout), "fp8": None, "scale": None}
+            gu.compare(got, want, "bf16", label=f"strided-graph-{path}-{step}")
+            assert np.all(_outside(ob, 8, H) == 0xFF) and np.all(_outside(rb, 8, H) == 0xFF)
