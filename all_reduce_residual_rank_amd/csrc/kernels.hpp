@@ -425,17 +425,16 @@ ARRMS_DEV u32x2 quant8_e4m3(const float (&y)[8], float scale, float inv, bool fa
     return q;
 }
 
-// max |y| of 8 values as fp32 bits: for non-negative floats the integer order
-// is the float order, and a NaN (bits above the infinity's) wins
-ARRMS_DEV uint32_t absmax_bits(const float (&y)[8])
+// max |y| of a pack of 8 T values, as T bits: with the sign cleared the
+// integer order of the bits is the order of |y| (a NaN ranks above infinity);
+// two 16-bit lanes per word
+ARRMS_DEV uint32_t absmax_tbits(const u32x4 &yv)
 {
-    uint32_t m = 0;
+    u16x2 m = {0, 0};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t b = __float_as_uint(y[e]) & 0x7fffffffu;
-        m = b > m ? b : m;
-    }
-    return m;
+    for (int i = 0; i < 4; ++i)
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, yv[i] & 0x7fff7fffu));
+    return m.x > m.y ? m.x : m.y;
 }
 
 // max over aligned groups of N lanes (N = 4 or 16) by DPP within 16-lane rows;
@@ -630,11 +629,9 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
         }
         const double rstd = 1.0 / __builtin_sqrt(ss / (double)a.H + (double)a.eps);
         // per-token FP8: the T-rounded y of every pack is kept for the quant,
-        // which needs the row's max |y|; the maximum is taken on the T bits
-        // with the sign cleared (their integer order is the order of |y|, and
-        // a NaN ranks above infinity), two 16-bit lanes per word
+        // which needs the row's max |y| (taken on the T bits, absmax_tbits)
         u32x4 yk[FP8 ? PPT : 1];
-        u16x2 ym = {0, 0};
+        uint32_t ym = 0;
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
             const uint32_t off = (uint32_t)(c.lt + k * c.tpr) * 16u;
@@ -694,9 +691,8 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
                     bstore(yv, rout_t, off);
             if constexpr (FP8 && DT != DT_FP32) {
                 yk[k] = yv;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    ym = __builtin_elementwise_max(ym, __builtin_bit_cast(u16x2, yv[i] & 0x7fff7fffu));
+                const uint32_t t = absmax_tbits(yv);
+                ym = t > ym ? t : ym;
             }
             if constexpr (GROUPQ && DT != DT_FP32) {
                 float y[8];
@@ -710,7 +706,9 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
                 const int pack = c.lt + k * c.tpr;  // pack index in the row
                 if constexpr (EPI == EPI_FP8G) {
                     // group max over the 16 lanes holding a group's 16 packs
-                    const float gmax = __uint_as_float(group_max_u32<16>(absmax_bits(y)));
+                    float gm[EPW];
+                    F::unpack(group_max_u32<16>(absmax_tbits(yv)), gm);  // the T value in the low half
+                    const float gmax = gm[0];
                     const float gscale = gmax / 448.0f;
                     const bool gfast = !exact_only && gscale >= 1.17549435e-38f && gscale <= 3.0e38f;
                     bstore8(quant8_e4m3(y, gscale, 1.0f / gscale, gfast), rout_q, off / 2u);
@@ -718,8 +716,9 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
                         ((float *)a.q_scale)[row * a.qgroups + (pack >> 4)] = gscale;
                 } else {
                     // MXFP4: block max over the 4 lanes holding a block's 4 packs
-                    const uint32_t am = group_max_u32<4>(absmax_bits(y));
-                    const uint32_t code = mx_scale_code(am);
+                    float bm[EPW];
+                    F::unpack(group_max_u32<4>(absmax_tbits(yv)), bm);
+                    const uint32_t code = mx_scale_code(__float_as_uint(bm[0]));
                     bstore4(mx_pack8(y, code), rout_q, off / 4u);
                     if ((pack & 3) == 0 && pack < c.P && row < a.M)
                         ((uint8_t *)a.q_scale)[row * a.qgroups + (pack >> 2)] = (uint8_t)code;
@@ -729,7 +728,7 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
         if constexpr (FP8 && DT != DT_FP32) {
             // the row's max |y|: wave tree, then the row group's waves via LDS
             // (a second barrier; the row's waves have all read red by then)
-            uint32_t am = wave_max_u32(ym.x > ym.y ? ym.x : ym.y);
+            uint32_t am = wave_max_u32(ym);
             if (c.wpr > 1) {
                 if (c.lane == 0)
                     redm[c.wave] = am;
