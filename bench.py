@@ -344,7 +344,20 @@ def cpu_baseline(wl, budget_s):
     tm = statistics.median(tt)
     out["threads"] = {"value": round(metric_bytes / tm / 1e9, 4), "cores": n,
                       "sample": f"the same rows split over {n} threads, median of 3 runs, {tm * 1e3:.1f} ms each"}
+    out["cpu_model"] = cpu_model()
     return out
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo, or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
