@@ -47,6 +47,19 @@ uintptr_t span_bytes(int M, int H, long long ld, int e)
     return (uintptr_t)(M - 1) * (uintptr_t)ld * (uintptr_t)e + (uintptr_t)H * (uintptr_t)e;
 }
 
+// No operand may span more than 2^48 bytes (far beyond any device memory):
+// with that bound every byte offset the kernels form fits in 64 bits.
+constexpr long long kMaxSpanBytes = 1ll << 48;
+
+// Whether M rows of H elements (e bytes each) at row stride ld (>= H >= 1)
+// span at most kMaxSpanBytes, computed without overflow.
+bool span_fits(long long M, long long H, long long ld, int e)
+{
+    if (ld > kMaxSpanBytes / e || H > ld)
+        return false;
+    return M <= 1 || (M - 1) <= (kMaxSpanBytes - H * e) / (ld * e);
+}
+
 // Quantised outputs: none, per-token FP8 (ARRMS_FP8), per-group FP8, MXFP4.
 enum Quant { Q_NONE = 0, Q_TOKEN = 1, Q_GROUP = 2, Q_MX = 3 };
 
@@ -98,7 +111,7 @@ int validate(const void *const *rank_in, int R, const void *residual, const void
     const int e = esize(dt);
     const long long lds[4] = {ld.in, ld.res, ld.out, ld.rout};
     for (int i = 0; i < 4; ++i) {
-        if (lds[i] < H)
+        if (lds[i] < H || !span_fits(M, H, lds[i], e))
             return ARRMS_ERR_INVALID;
         if ((lds[i] * e) % 16 != 0)
             return ARRMS_ERR_UNSUPPORTED;
@@ -107,7 +120,7 @@ int validate(const void *const *rank_in, int R, const void *residual, const void
         // codes go out 8 bytes per pack (E4M3) or 4 (packed E2M1): rows must
         // start aligned to that
         const long long qrow = quant == Q_MX ? H / 2 : H;
-        if (ld.q < qrow)
+        if (ld.q < qrow || !span_fits(M, qrow, ld.q, 1))
             return ARRMS_ERR_INVALID;
         if (ld.q % (quant == Q_MX ? 4 : 8) != 0)
             return ARRMS_ERR_UNSUPPORTED;
@@ -602,6 +615,8 @@ int arrms_allreduce_sum(const void *const *rank_in, int R, void *out, long long 
         return ARRMS_ERR_INVALID;
     const int dt = flags & ARRMS_DTYPE_MASK;
     if (dt > DT_FP32 || R < 1 || R > ARRMS_MAX_RANKS || n < 0 || !rank_in || !out)
+        return ARRMS_ERR_INVALID;
+    if (n > kMaxSpanBytes / esize(dt))
         return ARRMS_ERR_INVALID;
     for (int r = 0; r < R; ++r)
         if (!rank_in[r])
