@@ -132,8 +132,9 @@ ARRMS_API int arrms_fused(const void *const *rank_in, int R, const void *residua
  * all counted in elements of T, and ld_fp8 for fp8_out, counted in bytes
  * (ignored without ARRMS_FP8). Only the first H elements of each row are read
  * or written: the padding between rows is never touched. Every stride is at
- * least H (else ARRMS_ERR_INVALID) and spans a multiple of 16 bytes, ld_fp8 a
- * multiple of 8 bytes (else ARRMS_ERR_UNSUPPORTED). In place (residual_out == residual) requires
+ * least H and no matrix spans more than 2^48 bytes (else ARRMS_ERR_INVALID);
+ * every stride spans a multiple of 16 bytes, ld_fp8 a multiple of 8 bytes
+ * (else ARRMS_ERR_UNSUPPORTED). In place (residual_out == residual) requires
  * ld_residual_out == ld_residual. Overlap is judged on each matrix's whole
  * byte range, first element to last, padding included. Everything else --
  * arguments, results, paths, staging and error behaviour -- is arrms_fused's;
@@ -189,8 +190,9 @@ ARRMS_API int arrms_fused_quant(const void *const *rank_in, int R, const void *r
  * R        1 .. ARRMS_MAX_RANKS.
  * out      device n elements of T; may equal one of the rank pointers
  *          exactly (in place), must not overlap any of them otherwise.
- * n        elements, >= 0 (0: returns ARRMS_OK, launches nothing), with
- *          n * sizeof(T) % 16 == 0 (else ARRMS_ERR_UNSUPPORTED).
+ * n        elements, >= 0 (0: returns ARRMS_OK, launches nothing), at most
+ *          2^48 bytes (else ARRMS_ERR_INVALID), with n * sizeof(T) % 16 == 0
+ *          (else ARRMS_ERR_UNSUPPORTED).
  * flags    ARRMS_DTYPE_* only; any other bit gives ARRMS_ERR_INVALID.
  * stream   HIP stream; one kernel launch, asynchronous, no allocation, no
  *          shared state (safe in graph capture and on concurrent streams).
