@@ -363,7 +363,7 @@ def cpu_model():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+        print(json.dumps({"error": "the benchmark measures one GPU's share of the collective; run with --gpus 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
