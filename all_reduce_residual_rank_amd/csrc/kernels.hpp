@@ -533,7 +533,8 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
     // w_eff = w + gadd: 1 under gemma_norm, else -0.0, which adds nothing to
     // any value (signed zeros included), so one fp64 add serves both modes
     const double gadd = a.gemma ? 1.0 : -0.0;
-    // plain weights with 16-bit data: the product h * w needs no fp64
+    // plain weights with 16-bit data: h * w needs no gemma add (and, for
+    // fp16, no fp64 product)
     const bool plain_product = DT != DT_FP32 && !a.gemma;
     const bool exact_only = a.exact_only != 0;
     const int rb = c.P * 16;
@@ -641,8 +642,12 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
             // bits for the other lanes), so the branch stays wave-uniform
             uint64_t risk = exact_only ? ~0ull : 0ull;
             if (plain_product) {
-                // h * w is exact in fp32 (at most 8 + 8 or 11 + 11 significant bits),
-                // so fl64(h * w) = (double)(h * w): one conversion instead of two
+                // fp16: h * w is exact in fp32 (11 + 11 significant bits, and
+                // fp16's range keeps the product inside fp32's normal range), so
+                // fl64(h * w) = (double)(h * w): one conversion instead of two.
+                // bf16 shares fp32's exponent range: an fp32 product can overflow
+                // or lose bits below 2^-126 where h * w * rstd is an ordinary
+                // number, so the product is formed in fp64 (exact: 8 + 8 bits).
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float hf[EPW], wf[EPW], yf[EPW];
@@ -650,7 +655,10 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
                     F::unpack(w[k][i], wf);
 #pragma unroll
                     for (int e = 0; e < EPW; ++e) {
-                        yf[e] = (float)((double)(hf[e] * wf[e]) * rstd);
+                        if constexpr (DT == DT_BF16)
+                            yf[e] = (float)(((double)hf[e] * (double)wf[e]) * rstd);
+                        else
+                            yf[e] = (float)((double)(hf[e] * wf[e]) * rstd);
                         risk |= F::tie_mask(yf[e]);
                     }
                     yv[i] = F::pack(yf);
