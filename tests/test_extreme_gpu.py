@@ -101,3 +101,69 @@ def test_extreme_exponents_match_oracle(kind, fp8, path):
     if fp8:
         assert np.array_equal(got["scale"].view(np.uint32), want["scale"].view(np.uint32)), f"{label}: scales differ"
         assert np.array_equal(got["fp8"], want["fp8"]), f"{label}: {(got['fp8'] != want['fp8']).sum()} codes differ"
+
+
+# ---- all-zero rows with eps = 0: rstd = 1/sqrt(0) = inf and y = 0 * w * inf is
+# NaN in every column (IEEE arithmetic, as the oracle reads it); the other
+# rows are ordinary. Every output form, both paths; NaN payloads and signs are
+# not part of the reading, so T values and fp32 scales compare as "NaN at the
+# same places, equal bits elsewhere", codes and E8M0 scales exactly.
+QFLAG = {0: 0, 1: oracle.FP8, 2: oracle.FP8_GROUP, 3: oracle.MXFP4}
+INF = {"bf16": 0x7F80, "fp16": 0x7C00}
+
+
+def _same_t(got, want, dtype, label):
+    gn, wn = (got & 0x7FFF) > INF[dtype], (want & 0x7FFF) > INF[dtype]
+    assert np.array_equal(gn, wn), f"{label}: NaN positions differ"
+    assert np.array_equal(got[~wn], want[~wn]), f"{label}: {(got[~wn] != want[~wn]).sum()} values differ"
+
+
+@pytest.mark.parametrize("path", ["one", "two"])
+@pytest.mark.parametrize("quant", [0, 1, 2, 3], ids=["t", "fp8", "fp8group", "mxfp4"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_zero_rows_eps0_match_oracle(dtype, quant, path):
+    T = gu.TORCH_T[dtype]
+    g = torch.Generator().manual_seed(11)
+    xs = [torch.randn(M, H, generator=g).to(T) for _ in range(R)]
+    res = torch.randn(M, H, generator=g).to(T)
+    w = (torch.randn(H, generator=g) * 0.1 + 1.0).to(T)
+    for r in (1, 4):
+        for x in xs:
+            x[r] = 0
+        res[r] = 0
+    print(f"zero rows eps=0 {dtype} quant={quant} path={path}", flush=True)
+    want = oracle.fused([gu.host_bits(x) for x in xs], gu.host_bits(res), gu.host_bits(w), 0.0,
+                        wlmod.DT_CODE[dtype] | QFLAG[quant], want_out=True)
+    dev = torch.device("cuda")
+    xd = [x.to(dev) for x in xs]
+    rd, wd = res.to(dev), w.to(dev)
+    out = gu.poison_(torch.empty(M, H, dtype=T, device=dev))
+    rout = gu.poison_(torch.empty(M, H, dtype=T, device=dev))
+    flags = wlmod.DT_CODE[dtype] | PATHS[path]
+    q = sc = None
+    if quant == 0:
+        arrms.arrms_fused(xd, rd, wd, out, rout, eps=0.0, flags=flags)
+    else:
+        q = gu.poison_(torch.empty((M, H // 2) if quant == 3 else (M, H), dtype=torch.uint8, device=dev))
+        if quant == 1:
+            sc = gu.poison_(torch.empty(M, dtype=torch.float32, device=dev))
+        elif quant == 2:
+            sc = gu.poison_(torch.empty(M, H // 128, dtype=torch.float32, device=dev))
+        else:
+            sc = gu.poison_(torch.empty(M, H // 32, dtype=torch.uint8, device=dev))
+        arrms.arrms_fused_quant(xd, rd, wd, out, rout, q, sc, eps=0.0, flags=flags, quant=quant)
+    torch.cuda.synchronize()
+    label = f"zero rows {dtype}/q{quant}/{path}"
+    assert np.array_equal(gu.host_bits(rout), want["residual_out"]), f"{label}: residual_out differs"
+    got_out = gu.host_bits(out)
+    assert ((want["out"][1] & 0x7FFF) > INF[dtype]).all(), "a zero row normalises to NaN with eps = 0"
+    _same_t(got_out, want["out"], dtype, label + " out")
+    if quant:
+        assert np.array_equal(gu.host_bits(q), want["fp8"]), f"{label}: code bytes differ"
+        gs, ws = gu.host_bits(sc), want["scale"]
+        if quant == 3:
+            assert np.array_equal(gs, ws), f"{label}: E8M0 scales differ"
+        else:
+            gn, wn = np.isnan(gs), np.isnan(ws)
+            assert np.array_equal(gn, wn), f"{label}: NaN scales differ"
+            assert np.array_equal(gs[~wn].view(np.uint32), ws[~wn].view(np.uint32)), f"{label}: scales differ"
