@@ -425,7 +425,7 @@ bool apply_shape(const ShapeReq *req, int P, int R, long long M, arrms::RowShape
     if (s.rpb < 1 || s.tpr * s.rpb > max_block)
         return false;
     s.grid = req->grid;
-    if (req->window < 0 || req->window > 2)
+    if (req->window < 0 || req->window > 3)
         return false;
     s.window = req->window;
     return true;
@@ -588,7 +588,7 @@ int arrms_fused_config(const void *const *rank_in, int R, const void *residual, 
                        float eps, int flags, int ppt, int tpr, int rows_per_block, int blocks,
                        int load_window, hipStream_t stream)
 {
-    if (ppt < 0 || tpr < 0 || rows_per_block < 0 || blocks < 0 || load_window < 0 || load_window > 2)
+    if (ppt < 0 || tpr < 0 || rows_per_block < 0 || blocks < 0 || load_window < 0 || load_window > 3)
         return ARRMS_ERR_INVALID;
     const ShapeReq req = {ppt, tpr, rows_per_block, blocks, load_window};
     const Strides ld = {H, H, H, H, H};

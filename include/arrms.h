@@ -207,7 +207,7 @@ ARRMS_API int arrms_allreduce_sum(const void *const *rank_in, int R, void *out, 
 /*
  * arrms_fused_config -- arrms_fused with an explicit launch shape for the row
  * kernel, for benchmarking and tuning (the automatic choice is the shape
- * arrms_fused takes). ppt: 16-byte packs per thread and row (1, 2 or 4); tpr:
+ * arrms_fused takes). ppt: 16-byte packs per thread and row (1 to 4); tpr:
  * threads per row (a multiple of 64, tpr * ppt covering the row);
  * rows_per_block: rows handled side by side by one block (tpr *
  * rows_per_block at most 1024 threads with ppt = 1, else 512); blocks: the
@@ -215,8 +215,9 @@ ARRMS_API int arrms_allreduce_sum(const void *const *rank_in, int R, void *out, 
  * takes every blocks-th group of rows in turn; load_window: how many 16-byte
  * loads a thread keeps in flight -- 1 a narrow window (for large launches
  * whose rows are all resident at once), 2 a wide one (the whole row, up to a
- * cap). 0 in any of them keeps the automatic value; a negative value (or a
- * load_window above 2) gives ARRMS_ERR_INVALID and a shape that cannot cover
+ * cap: small launches), 3 a medium one (large launches that run in several
+ * rounds of blocks). 0 in any of them keeps the automatic value; a negative
+ * value (or a load_window above 3) gives ARRMS_ERR_INVALID and a shape that cannot cover
  * a row ARRMS_ERR_UNSUPPORTED. All other arguments, the results and the
  * error behaviour are arrms_fused's.
  */

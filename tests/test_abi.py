@@ -212,7 +212,8 @@ def test_fused_config_argument_checks():
             None, None, 0, 64, 1e-6, 0)
     assert arrms.arrms_fused_config_raw(*args, 0, 0, 0, 0, None) == arrms.OK
     assert arrms.arrms_fused_config_raw(*args, 0, 0, 0, 0, None, load_window=2) == arrms.OK
-    for bad in ((-1, 0, 0, 0, 0), (0, -64, 0, 0, 0), (0, 0, -1, 0, 0), (0, 0, 0, -5, 0), (0, 0, 0, 0, 3),
+    assert arrms.arrms_fused_config_raw(*args, 0, 0, 0, 0, None, load_window=3) == arrms.OK
+    for bad in ((-1, 0, 0, 0, 0), (0, -64, 0, 0, 0), (0, 0, -1, 0, 0), (0, 0, 0, -5, 0), (0, 0, 0, 0, 4),
                 (0, 0, 0, 0, -1)):
         ppt, tpr, rpb, blocks, win = bad
         assert arrms.arrms_fused_config_raw(*args, ppt, tpr, rpb, blocks, None, load_window=win) == \

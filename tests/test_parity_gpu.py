@@ -300,11 +300,12 @@ def _run_config(wl, xs, res, w, flags, ppt, tpr, rpb, blocks, window):
 
 # (ppt, tpr, rows_per_block, blocks, load_window): one row group per block,
 # row loops over a few blocks (every block takes several rows in turn),
-# several row groups side by side per block, wide one-pack blocks, and both
-# phase-1 load windows
+# several row groups side by side per block, wide one-pack blocks, and the
+# three phase-1 load windows
 SHAPES = [(0, 0, 0, 0, 0), (0, 0, 0, 7, 0), (0, 0, 0, 64, 1), (1, 0, 0, 5, 2), (2, 0, 0, 33, 1),
           (4, 0, 0, 3, 2), (2, 0, 2, 11, 2), (1, 0, 0, 1, 1), (4, 0, 0, 0, 1), (4, 0, 0, 0, 2),
-          (2, 0, 0, 0, 1), (1, 0, 0, 0, 2)]
+          (2, 0, 0, 0, 1), (1, 0, 0, 0, 2), (4, 0, 0, 0, 3), (3, 0, 0, 9, 3), (2, 0, 2, 0, 3),
+          (1, 0, 0, 0, 3)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "ppt%d-tpr%d-rpb%d-b%d-w%d" % s)
