@@ -57,7 +57,7 @@ struct FlatArgs {
 // rpb rows side by side per block; tail = tpr * PPT > packs per row. grid is
 // the number of blocks: 0 (or at least the number of row groups) gives one
 // block per group of rpb rows; fewer blocks each take every grid-th group in
-// turn. window: phase-1 load window, 0 automatic, 1 narrow, 2 wide.
+// turn. window: phase-1 load window, 0 automatic, 1 narrow, 2 wide, 3 medium.
 struct RowShape {
     int ppt;
     int tpr;
