@@ -627,9 +627,16 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
             out_stream(a.fp8_out, row, a.ld_q, EPI == EPI_MX4 ? rb / 4 : rb / 2, a.M);
         // a throttled row writes residual_out once the row is reduced: the
         // stores never count against the load window, and the row's reads
-        // are over before its writes begin (measured faster on MI355X)
-        if constexpr (W < NL || ARRMS_ROUT_LATE_ALL) {
-            const __amdgpu_buffer_rsrc_t rout = out_stream(a.residual_out, row, a.ld_rout, rb, a.M);
+        // are over before its writes begin (measured faster on MI355X). With
+        // the T output alone and 2 to 6 ranks they go later still, after the
+        // row's T output (1024 x 6144 bf16 rows: 0.27-0.53 us faster at R = 2
+        // to 4, 0.15 at R = 6; 0.3 us slower at R = 8 and 1 us slower for the
+        // R = 1 row pass of the two-stage path, which keep the earlier place;
+        // and slower for the per-token FP8 epilogue)
+        constexpr bool rout_late = W < NL || ARRMS_ROUT_LATE_ALL;
+        constexpr bool rout_after_y = rout_late && EPI == EPI_T && R >= 2 && R <= 6;
+        const __amdgpu_buffer_rsrc_t rout = out_stream(a.residual_out, row, a.ld_rout, rb, a.M);
+        if constexpr (rout_late && !rout_after_y) {
 #pragma unroll
             for (int k = 0; k < PPT; ++k)
                 bstore(hv[k], rout, (uint32_t)(c.lt + k * c.tpr) * 16u);
@@ -738,6 +745,11 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
                         ((uint8_t *)a.q_scale)[row * a.qgroups + (pack >> 2)] = (uint8_t)code;
                 }
             }
+        }
+        if constexpr (rout_after_y) {
+#pragma unroll
+            for (int k = 0; k < PPT; ++k)
+                bstore(hv[k], rout, (uint32_t)(c.lt + k * c.tpr) * 16u);
         }
         if constexpr (FP8 && DT != DT_FP32) {
             // the row's max |y|: wave tree, then the row group's waves via LDS

@@ -42,8 +42,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=256)
-    p.add_argument("--warmup", type=int, default=512,
-                   help="untimed calls first (enough for the clocks to settle)")
+    p.add_argument("--warmup", type=int, default=4096,
+                   help="untimed calls first: the per-call time keeps falling over the first ~500 "
+                        "calls (clocks and memory settling), so warm up well past that")
     p.add_argument("--workload", default="r4_m1024_h6144_bf16_rowscale")
     p.add_argument("--path", choices=("auto", "one", "two"), default="auto")
     p.add_argument("--no-cpu-baseline", action="store_true")
