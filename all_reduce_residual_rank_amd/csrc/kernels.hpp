@@ -536,6 +536,23 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
     constexpr int NS = R + 1;        // input streams
     constexpr int NL = PPT * NS;     // loads per thread and row
     constexpr int W = WIN < NL ? WIN : NL;
+    // Where residual_out is written. A row whose loads are throttled by the
+    // window writes it only after its reads are over (measured faster on
+    // MI355X: the DRAM gives more when a row's reads and writes do not
+    // interleave) -- after the row reduction, or, with the T output or a
+    // group quant output and 2 to 6 ranks, after the row's other outputs. The
+    // group quant epilogues do so even when every load of the row is in
+    // flight at once. Measured on 1024 x 6144 bf16 rows (T output): after the
+    // reduction 14.70-14.82 us, after the T output 14.41-14.47 (R = 2: 11.02
+    // -> 10.76, R = 3: 13.03 -> 12.50, R = 6: 21.70 -> 21.56); slower at R = 8
+    // (26.36 -> 26.66), for the R = 1 row pass of the two-stage path (+1 us per
+    // call) and for the per-token FP8 epilogue, which keep the earlier place.
+    // On 2800 x 6144 fp16 gemma rows the group forms gain 0.27 (per-group FP8)
+    // and 0.8 us (MXFP4); the T output with every load in flight loses 0.04-0.1
+    // us by waiting, so it writes residual_out pack by pack in phase 1.
+    constexpr bool mid_ranks = R >= 2 && R <= 6;
+    constexpr bool rout_late = W < NL || ARRMS_ROUT_LATE_ALL || (GROUPQ && mid_ranks);
+    constexpr bool rout_after_y = rout_late && (EPI == EPI_T || GROUPQ) && mid_ranks;
     // w_eff = w + gadd: 1 under gemma_norm, else -0.0, which adds nothing to
     // any value (signed zeros included), so one fp64 add serves both modes
     const double gadd = a.gemma ? 1.0 : -0.0;
@@ -592,7 +609,7 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
                 if (j >= 0 && j % NS == NS - 1) {
                     const int k = j / NS;
                     reduce_pack<DT, R>(x[k], hv[k], ssw);
-                    if constexpr (W == NL && !ARRMS_ROUT_LATE_ALL)
+                    if constexpr (!rout_late)
                         bstore(hv[k], out_stream(a.residual_out, row, a.ld_rout, rb, a.M),
                                (uint32_t)(c.lt + k * c.tpr) * 16u);
                 }
@@ -625,16 +642,7 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
         const __amdgpu_buffer_rsrc_t rout_t = out_stream(a.out, row, a.ld_out, rb, a.M);
         const __amdgpu_buffer_rsrc_t rout_q =
             out_stream(a.fp8_out, row, a.ld_q, EPI == EPI_MX4 ? rb / 4 : rb / 2, a.M);
-        // a throttled row writes residual_out once the row is reduced: the
-        // stores never count against the load window, and the row's reads
-        // are over before its writes begin (measured faster on MI355X). With
-        // the T output alone and 2 to 6 ranks they go later still, after the
-        // row's T output (1024 x 6144 bf16 rows: 0.27-0.53 us faster at R = 2
-        // to 4, 0.15 at R = 6; 0.3 us slower at R = 8 and 1 us slower for the
-        // R = 1 row pass of the two-stage path, which keep the earlier place;
-        // and slower for the per-token FP8 epilogue)
-        constexpr bool rout_late = W < NL || ARRMS_ROUT_LATE_ALL;
-        constexpr bool rout_after_y = rout_late && EPI == EPI_T && R >= 2 && R <= 6;
+        // residual_out of a late row (see rout_late above)
         const __amdgpu_buffer_rsrc_t rout = out_stream(a.residual_out, row, a.ld_rout, rb, a.M);
         if constexpr (rout_late && !rout_after_y) {
 #pragma unroll
