@@ -285,13 +285,14 @@ ARRMS_DEV void bstore4(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t off)
 // of kWindowLow loads per thread is that amount (more measured slower: the
 // DRAM pages of the many streams get interleaved; fewer starve the memory
 // pipeline). Large launches that run in several rounds of blocks take the
-// wide window (the whole row, up to kWindowHigh loads), except the per-token
-// FP8 epilogue, which takes the medium one (kWindowMid: measured 0.45 us
-// faster on 2800 x 6144 fp16 rows, 15 loads per thread; the per-group FP8
-// epilogue measured 0.2 us slower with it, MXFP4 and 18-load bf16 rows
-// equal); small launches take the wide window too, which issues every load
-// at once: a wait inside the row would add a memory round trip to their
-// latency.
+// wide window (the whole row, up to kWindowHigh loads), and so do small
+// launches, for which it issues every load at once: a wait inside the row
+// would add a memory round trip to their latency. A medium window
+// (kWindowMid) is there on explicit request: with residual_out written after
+// the row reduction it was 0.45 us faster than the wide one for the per-token
+// FP8 epilogue on 2800 x 6144 fp16 rows, but with residual_out after the
+// codes (as now) the wide window is 0.1 us faster still; it was 0.2 us slower
+// for per-group FP8 and equal for MXFP4 and for 18-load bf16 rows.
 #ifndef ARRMS_ROUT_LATE_ALL
 #define ARRMS_ROUT_LATE_ALL 0
 #endif
@@ -539,20 +540,22 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
     // Where residual_out is written. A row whose loads are throttled by the
     // window writes it only after its reads are over (measured faster on
     // MI355X: the DRAM gives more when a row's reads and writes do not
-    // interleave) -- after the row reduction, or, with the T output or a
-    // group quant output and 2 to 6 ranks, after the row's other outputs. The
-    // group quant epilogues do so even when every load of the row is in
-    // flight at once. Measured on 1024 x 6144 bf16 rows (T output): after the
-    // reduction 14.70-14.82 us, after the T output 14.41-14.47 (R = 2: 11.02
-    // -> 10.76, R = 3: 13.03 -> 12.50, R = 6: 21.70 -> 21.56); slower at R = 8
-    // (26.36 -> 26.66), for the R = 1 row pass of the two-stage path (+1 us per
-    // call) and for the per-token FP8 epilogue, which keep the earlier place.
-    // On 2800 x 6144 fp16 gemma rows the group forms gain 0.27 (per-group FP8)
-    // and 0.8 us (MXFP4); the T output with every load in flight loses 0.04-0.1
-    // us by waiting, so it writes residual_out pack by pack in phase 1.
+    // interleave) -- after the row reduction, or, with 2 to 6 ranks, after
+    // the row's other outputs (the T output, or the quantised codes). The
+    // quant epilogues do so even when every load of the row is in flight at
+    // once. Measured on 1024 x 6144 bf16 rows (T output): after the reduction
+    // 14.70-14.82 us, after the T output 14.41-14.47 (R = 2: 11.02 -> 10.76,
+    // R = 3: 13.03 -> 12.50, R = 6: 21.70 -> 21.56); slower at R = 8 (26.36 ->
+    // 26.66) and for the R = 1 row pass of the two-stage path (+1 us per
+    // call), which keep the earlier place. On 2800 x 6144 fp16 gemma rows the
+    // quant forms gain 0.17 (per-token FP8, against the medium window with
+    // residual_out after the reduction), 0.27 (per-group FP8) and 0.8 us
+    // (MXFP4); the T output with every load in flight loses 0.04-0.1 us by
+    // waiting, so it writes residual_out pack by pack in phase 1.
     constexpr bool mid_ranks = R >= 2 && R <= 6;
-    constexpr bool rout_late = W < NL || ARRMS_ROUT_LATE_ALL || (GROUPQ && mid_ranks);
-    constexpr bool rout_after_y = rout_late && (EPI == EPI_T || GROUPQ) && mid_ranks;
+    constexpr bool quant_out = FP8 || GROUPQ;
+    constexpr bool rout_late = W < NL || ARRMS_ROUT_LATE_ALL || (quant_out && mid_ranks);
+    constexpr bool rout_after_y = rout_late && (EPI == EPI_T || quant_out) && mid_ranks;
     // w_eff = w + gadd: 1 under gemma_norm, else -0.0, which adds nothing to
     // any value (signed zeros included), so one fp64 add serves both modes
     const double gadd = a.gemma ? 1.0 : -0.0;
@@ -754,7 +757,7 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
                 }
             }
         }
-        if constexpr (rout_after_y) {
+        if constexpr (rout_after_y && !FP8) {
 #pragma unroll
             for (int k = 0; k < PPT; ++k)
                 bstore(hv[k], rout, (uint32_t)(c.lt + k * c.tpr) * 16u);
@@ -790,6 +793,11 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
                     y[2 * i + 1] = t[1];
                 }
                 bstore8(quant8_e4m3(y, scale, inv, qfast), rout_q, (uint32_t)(c.lt + k * c.tpr) * 8u);
+            }
+            if constexpr (rout_after_y) {
+#pragma unroll
+                for (int k = 0; k < PPT; ++k)
+                    bstore(hv[k], rout, (uint32_t)(c.lt + k * c.tpr) * 16u);
             }
         }
     }
@@ -952,18 +960,15 @@ static hipError_t row_go(const RowArgs &a, const RowShape &s, hipStream_t st)
     b.groups = groups;
     int win = s.window;  // 1 narrow, 2 wide, 3 medium
     if (win == 0) {
-        // launches whose input streams exceed 16 MiB: the narrow window when
-        // the whole launch is resident at once (then the window, not the
-        // launch size, sets the bytes in flight), else the medium one for the
-        // per-token FP8 epilogue; the wide window for the others
+        // the narrow window when the whole launch is resident at once and its
+        // input streams exceed 16 MiB (then the window, not the launch size,
+        // sets the bytes in flight); the wide window for the others
         const long long input = (long long)(R + 1) * a.M * a.P * 16;
         win = 2;
         if (input > (16ll << 20)) {
             const long long resident = (long long)blocks_per_cu<DT, R, PPT, EPI>(block) * device_cus();
             if (grid <= resident)
                 win = 1;
-            else if (EPI == EPI_FP8 || EPI == EPI_FP8_T)
-                win = 3;
         }
     }
     const dim3 g((unsigned)grid), t((unsigned)block);

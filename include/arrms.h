@@ -215,8 +215,9 @@ ARRMS_API int arrms_allreduce_sum(const void *const *rank_in, int R, void *out, 
  * takes every blocks-th group of rows in turn; load_window: how many 16-byte
  * loads a thread keeps in flight -- 1 a narrow window (for large launches
  * whose rows are all resident at once), 2 a wide one (the whole row, up to a
- * cap: small launches), 3 a medium one (large launches that run in several
- * rounds of blocks). 0 in any of them keeps the automatic value; a negative
+ * cap: small launches, and large ones that run in several rounds of
+ * blocks), 3 a medium one (8 loads; an alternative for the latter). 0 in any
+ * of them keeps the automatic value; a negative
  * value (or a load_window above 3) gives ARRMS_ERR_INVALID and a shape that cannot cover
  * a row ARRMS_ERR_UNSUPPORTED. All other arguments, the results and the
  * error behaviour are arrms_fused's.
