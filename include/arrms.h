@@ -217,10 +217,10 @@ ARRMS_API int arrms_allreduce_sum(const void *const *rank_in, int R, void *out, 
  * whose rows are all resident at once), 2 a wide one (the whole row, up to a
  * cap: small launches, and large ones that run in several rounds of
  * blocks), 3 a medium one (8 loads; an alternative for the latter). 0 in any
- * of them keeps the automatic value; a negative
- * value (or a load_window above 3) gives ARRMS_ERR_INVALID and a shape that cannot cover
- * a row ARRMS_ERR_UNSUPPORTED. All other arguments, the results and the
- * error behaviour are arrms_fused's.
+ * of them keeps the automatic value; a negative value (or a load_window
+ * above 3) gives ARRMS_ERR_INVALID and a shape that cannot cover a row
+ * ARRMS_ERR_UNSUPPORTED. All other arguments, the results and the error
+ * behaviour are arrms_fused's.
  */
 ARRMS_API int arrms_fused_config(const void *const *rank_in, int R, const void *residual,
                                  const void *weight, void *out, void *residual_out, void *fp8_out,
