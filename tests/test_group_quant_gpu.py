@@ -93,6 +93,19 @@ def test_group_quant_matches_oracle(wl, quant, path):
         _check(got, want, f"{wl.name}/q{quant}/{path}/mirror{mirror}")
 
 
+# every R: with 2 to 6 ranks the group forms write residual_out after their
+# codes, otherwise pack by pack (or after the reduction when the window throttles)
+@pytest.mark.parametrize("path", ["one", "two"])
+@pytest.mark.parametrize("quant", [2, 3], ids=["fp8group", "mxfp4"])
+@pytest.mark.parametrize("R", range(1, 9))
+def test_group_quant_every_rank_count(R, quant, path):
+    wl = wlmod.Workload(f"q_rsweep_r{R}", R=R, M=200, H=6144, dtype="fp16", gemma=True, w_mean=0.0)
+    xs, res, w = wlmod.make_inputs(wl, seed=60 + R)
+    want = _oracle(wl, xs, res, w, quant, False)
+    got = _run(wl, xs, res, w, quant, path, False)
+    _check(got, want, f"{wl.name}/q{quant}/{path}")
+
+
 @pytest.mark.parametrize("wl", [wlmod.Workload("mx_2880", R=4, M=121, H=2880),
                                 wlmod.Workload("mx_fp16_96", R=2, M=40, H=96, dtype="fp16")],
                          ids=lambda w: w.name)

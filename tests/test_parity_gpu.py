@@ -124,6 +124,21 @@ def test_every_rank_count(R, dtype):
     _case(wl, R, ("one", "two"))
 
 
+# every R at a size whose rows are all resident at once with inputs above
+# 16 MiB: the narrow load window, where residual_out is written after the
+# reduction (R = 1, 7, 8) or after the row's other outputs (R = 2 to 6); the T
+# output in bf16 and per-token FP8 (with the mirror) in fp16
+@pytest.mark.parametrize("R", range(1, 9))
+@pytest.mark.parametrize("kind", ["bf16_t", "fp16_fp8"])
+def test_every_rank_count_resident_rows(R, kind):
+    if kind == "bf16_t":
+        wl = wlmod.Workload("rsweep_resident", R=R, M=1024, H=6144, row_scale=(0.1, 10.0))
+    else:
+        wl = wlmod.Workload("rsweep_resident_fp8", R=R, M=1024, H=6144, dtype="fp16", gemma=True, fp8=True,
+                            mirror=True, w_mean=0.0)
+    _case(wl, 40 + R, ("one", "two"))
+
+
 @pytest.mark.parametrize("H", [8, 16, 64, 136, 504, 520, 1016, 3072, 5120, 8200, 16384])
 def test_hidden_sizes_and_tails(H):
     wl = wlmod.Workload("hsweep", R=3, M=19, H=H, dtype="bf16", fp8=True, mirror=True)
