@@ -139,6 +139,14 @@ def test_every_rank_count_resident_rows(R, kind):
     _case(wl, 40 + R, ("one", "two"))
 
 
+# launches of 6 or more input streams that run in several rounds of blocks
+# (occupancy capped at 16 waves per compute unit)
+@pytest.mark.parametrize("R", [5, 6, 7])
+def test_capped_occupancy_rows(R):
+    wl = wlmod.Workload("capped", R=R, M=2048, H=7168, eps=1e-5)
+    _case(wl, 50 + R, ("one",))
+
+
 @pytest.mark.parametrize("H", [8, 16, 64, 136, 504, 520, 1016, 3072, 5120, 8200, 16384])
 def test_hidden_sizes_and_tails(H):
     wl = wlmod.Workload("hsweep", R=3, M=19, H=H, dtype="bf16", fp8=True, mirror=True)
