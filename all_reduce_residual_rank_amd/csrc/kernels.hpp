@@ -1005,10 +1005,13 @@ static hipError_t row_go(const RowArgs &a, const RowShape &s, hipStream_t st)
     const long long resident = large ? (long long)blocks_per_cu<DT, R, PPT, EPI>(block) * device_cus() : 0;
     int win = s.window;  // 1 narrow, 2 wide, 3 medium
     if (win == 0) {
-        // the narrow window when the whole launch is resident at once and its
+        // the narrow window when the whole launch is resident at once, its
         // input streams exceed 16 MiB (then the window, not the launch size,
-        // sets the bytes in flight); the wide window for the others
-        win = large && grid <= resident ? 1 : 2;
+        // sets the bytes in flight) and a row has at most 6 of them; the wide
+        // window for the others (resident 1024 x 6144 bf16 rows: R = 5 17.8
+        // us narrow, 19.0 wide; R = 6 21.4 narrow, 21.0 wide; R = 8 25.1
+        // narrow, 24.7 wide)
+        win = large && grid <= resident && R <= 5 ? 1 : 2;
     }
     // A large launch of 6 or more input streams per row that runs in several
     // rounds of blocks with the wide window: at most 16 waves per compute
