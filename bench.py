@@ -18,6 +18,8 @@ Prints one JSON line:
   allreduce_sum the plain rank all-reduce (no norm) over a message of the same
               rank inputs' size (4 x 1024 x 6144 bf16), with its own roofline
               fraction; --sum-only prints that measurement as the line instead
+  copy_reference a plain 256 MiB device-to-device copy on the same GPU (read
+              plus written bytes per second), for context
 """
 from __future__ import annotations
 
@@ -55,6 +57,8 @@ def parse():
     p.add_argument("--no-sum", action="store_true",
                    help="skip the plain rank all-reduce (no norm) timing")
     p.add_argument("--no-strided", action="store_true", help="skip the padded-rows timing")
+    p.add_argument("--no-copy-reference", action="store_true",
+                   help="skip the plain 256 MiB device copy timed for reference")
     p.add_argument("--no-quant", action="store_true",
                    help="skip the per-token / per-group FP8 / MXFP4 epilogue timings")
     p.add_argument("--replays", type=int, default=20,
@@ -169,6 +173,28 @@ def time_graph(torch, calls, steps, warmup, extra=None):
 def time_path(torch, arrms, wl, sets, flags, steps, warmup, extra=None):
     calls = [lambda st, d=d: call(arrms, wl, d, flags, st) for d in sets.sets]
     return time_graph(torch, calls, steps, warmup, extra)
+
+
+def copy_reference(torch, nbytes=256 << 20, reps=10):
+    """A plain device-to-device copy (torch's copy_) of nbytes on this GPU, as a
+    reference for what a simple one-stream streaming kernel reaches here: GB/s
+    counting the bytes read and the bytes written."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / reps
+    del src, dst
+    return {"kind": "torch copy_ device to device", "bytes_per_copy": 2 * nbytes, "us_per_copy": round(us, 2),
+            "achieved": round(2 * nbytes / (us * 1e-6) / 1e9, 1), "unit": "GB/s"}
 
 
 def time_strided(torch, arrms, wl, pad, steps, warmup):
@@ -480,6 +506,9 @@ def main():
                           "achieved": round(q_bytes / (q_us * 1e-6) / 1e9, 2),
                           "frac": round(q_bytes / (q_us * 1e-6) / 1e9 / PEAK_GBS, 4)}
         line["quant_epilogues"] = {"workload": qwl.name, "unit": "GB/s", "kernel": "row_kernel", **qres}
+    if not args.no_copy_reference and not args.calibrate_copy:
+        # (not in profiling runs: their counters are scaled by the one calibration copy)
+        line["copy_reference"] = copy_reference(torch)
     clocks = read_clocks(torch)
     if clocks:
         line["clocks"] = clocks
