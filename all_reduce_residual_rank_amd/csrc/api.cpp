@@ -510,9 +510,13 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
         staging_bytes = g_staging[dev].bytes;
     }
     const size_t row_bytes = (size_t)H * (size_t)e;
-    long long chunk = (long long)(staging_bytes / row_bytes);
-    if (chunk < 1)
+    const long long cap = (long long)(staging_bytes / row_bytes);  // rows the staging holds
+    if (cap < 1)
         return ARRMS_ERR_NO_STAGING;
+    // chunks of equal size (at most cap rows each): no small last chunk, whose
+    // two launches would run a short, latency-bound round of blocks
+    const long long nchunks = (M + cap - 1) / cap;
+    const long long chunk = (M + nchunks - 1) / nchunks;
     for (long long m0 = 0; m0 < M; m0 += chunk) {
         const long long n = (M - m0) < chunk ? (M - m0) : chunk;
         arrms::FlatArgs f;
