@@ -208,8 +208,10 @@ int choose_path(int M, int H, int R, int flags)
 // least padding, then more packs per thread (fewer, busier threads: measured
 // faster on MI355X for large launches) as long as a thread's R+1 input packs
 // stay within 20 (80 registers). Launches of fewer than 512 rows cap PPT at 2
-// (more threads per row make up for the few rows), and the FP8 epilogue, with
-// more per-element work after the row reduction, caps it at 3.
+// (more threads per row make up for the few rows), launches of fewer than 64
+// rows of 513 to 1024 packs take one pack per thread (blocks of up to 1024
+// threads), and the FP8 epilogue, with more per-element work after the row
+// reduction, caps PPT at 3.
 arrms::RowShape choose_shape(int P, int R, long long M, bool fp8)
 {
     arrms::RowShape best = {0, 0, 0, false, 0, 0};
@@ -217,6 +219,12 @@ arrms::RowShape choose_shape(int P, int R, long long M, bool fp8)
     int cap = fp8 ? 3 : 4;
     if (M < 512 && cap > 2)
         cap = 2;
+    // a handful of wide rows (each on its own compute unit, latency-bound): one
+    // pack per thread, the most waves per row (16 x 6144 bf16: 4.32 us against
+    // 4.45-4.47 with two packs per thread; rows of at most 512 packs gain
+    // nothing: 1 x 2880 and 64 x 2880 equal either way)
+    if (M < 64 && P > 512 && P <= 1024)
+        cap = 1;
     const int ppts[4] = {1, 2, 3, 4};
     for (int c = 0; c < 4; ++c) {
         const int ppt = ppts[c];
@@ -226,7 +234,7 @@ arrms::RowShape choose_shape(int P, int R, long long M, bool fp8)
             continue;
         int tpr = (P + ppt - 1) / ppt;
         tpr = (tpr + 63) / 64 * 64;
-        if (tpr > 512)
+        if (tpr > (cap == 1 ? 1024 : 512))  // one pack per thread: blocks of up to 1024
             continue;
         const int waste = tpr * ppt - P;
         const long long key = (long long)waste * 16 + (4 - ppt);
