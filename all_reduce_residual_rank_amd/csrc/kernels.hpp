@@ -299,7 +299,13 @@ ARRMS_DEV void bstore4(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t off)
 #ifndef ARRMS_LATE_WEIGHTS
 #define ARRMS_LATE_WEIGHTS 1
 #endif
-constexpr int kWindowLow = 3;
+// The narrow window: 2 loads per thread; 3 for the two-stage row pass (R = 1).
+// Measured on 1024 x 6144 rows with residual_out written after the T output:
+// R = 4 14.34 -> 14.13-14.15 us from 3 to 2 (4: 14.33-14.35), R = 3 12.40 ->
+// 12.29, R = 2 10.65 -> 10.61; the R = 1 row pass was 1.5 us slower at 2.
+constexpr int kWindowLow = 2;
+constexpr int kWindowLowR1 = 3;
+template <int R> constexpr int window_low() { return R == 1 ? kWindowLowR1 : kWindowLow; }
 constexpr int kWindowMid = 8;
 constexpr int kWindowHigh = 16;
 
@@ -970,7 +976,7 @@ static void device_lds(int &per_cu, int &per_block)
     per_block = b;
 }
 
-// Blocks of row_kernel<.., kWindowLow> one compute unit holds at this block
+// Blocks of row_kernel<.., window_low<R>()> one compute unit holds at this block
 // size (cached per block size; 0 if the runtime cannot tell).
 template <int DT, int R, int PPT, int EPI>
 static int blocks_per_cu(int block)
@@ -979,7 +985,7 @@ static int blocks_per_cu(int block)
     const int slot = block / 64;
     int n = cache[slot].load(std::memory_order_relaxed);
     if (n == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_kernel<DT, R, PPT, EPI, kWindowLow>, block, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_kernel<DT, R, PPT, EPI, window_low<R>()>, block, 0) !=
             hipSuccess) {
             (void)hipGetLastError();
             return 0;
@@ -1033,7 +1039,7 @@ static hipError_t row_go(const RowArgs &a, const RowShape &s, hipStream_t st)
     }
     const dim3 g((unsigned)grid), t((unsigned)block);
     if (win == 1) {
-        hipLaunchKernelGGL((row_kernel<DT, R, PPT, EPI, kWindowLow>), g, t, 0, st, b);
+        hipLaunchKernelGGL((row_kernel<DT, R, PPT, EPI, window_low<R>()>), g, t, 0, st, b);
     } else if (win == 3) {
         // rows of at most kWindowMid loads per thread: the medium window is the wide one
         if constexpr ((R + 1) * PPT > kWindowMid)
