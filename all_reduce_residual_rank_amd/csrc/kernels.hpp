@@ -284,8 +284,10 @@ ARRMS_DEV void bstore4(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t off)
 // the device. When every row of a large launch is resident at once, a window
 // of kWindowLow loads per thread is that amount (more measured slower: the
 // DRAM pages of the many streams get interleaved; fewer starve the memory
-// pipeline). Large launches that run in several rounds of blocks take the
-// wide window (the whole row, up to kWindowHigh loads), and so do small
+// pipeline) -- for rows of at most 6 input streams; rows of more (R > 5)
+// measured faster with the wide window. Large launches that run in several
+// rounds of blocks take the wide window (the whole row, up to kWindowHigh
+// loads), and so do small
 // launches, for which it issues every load at once: a wait inside the row
 // would add a memory round trip to their latency. A medium window
 // (kWindowMid) is there on explicit request: with residual_out written after
