@@ -1036,7 +1036,9 @@ static hipError_t row_go(const RowArgs &a, const RowShape &s, hipStream_t st)
         device_lds(lds_cu, lds_block);
         const int cap = 1024 / block;  // blocks per compute unit for 16 waves
         const size_t want = (size_t)lds_cu / (size_t)(cap + 1) + 1;  // cap + 1 blocks do not fit
-        if (cap >= 1 && lds_cu > 0 && want <= (size_t)lds_block)
+        // blocks of at most 512 threads (cap >= 2): the reservation stays below
+        // 64 KiB, which a launch may take without a per-kernel attribute
+        if (cap >= 2 && lds_cu > 0 && want <= (size_t)lds_block && want <= (64u << 10))
             smem = (want + 255) & ~(size_t)255;
     }
     const dim3 g((unsigned)grid), t((unsigned)block);
