@@ -40,7 +40,7 @@ FORCE_TWO_STAGE = 32
 EXACT_ONLY = 64
 MAX_RANKS = 8
 MAX_HIDDEN = 16384
-MAX_ROW_BYTES = 32768
+MAX_ROW_BYTES = 65536
 DEFAULT_STAGING_BYTES = 16 << 20
 PATH_NONE, PATH_ONE_STAGE, PATH_TWO_STAGE = 0, 1, 2
 
@@ -101,6 +101,60 @@ def _addr(t) -> int | None:
     return t.data_ptr()
 
 
+_T_BY_CODE = {DTYPE_BF16: "bfloat16", DTYPE_FP16: "float16", DTYPE_FP32: "float32"}
+
+
+def _check(t, name: str, *, dtype=None, numel: int = 0, nbytes: int = 0, contiguous: bool = True,
+           device=None) -> None:
+    """Host-side check of one tensor argument before its address goes to the C
+    ABI: a GPU tensor (on `device` when given), of `dtype` (a torch dtype name,
+    or None for any), contiguous when asked, holding at least `numel` elements
+    or `nbytes` bytes from its first element on. Ints (raw addresses) and None
+    pass unchecked. Raises ValueError."""
+    if t is None or isinstance(t, int):
+        return
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
+    if dtype is not None and str(t.dtype) != f"torch.{dtype}":
+        raise ValueError(f"{name} must be {dtype} for these flags (got {t.dtype})")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (use arrms_fused_strided for padded rows)")
+    have = t.untyped_storage().nbytes() - t.storage_offset() * t.element_size()
+    need = max(numel * t.element_size(), nbytes)
+    if have < need:
+        raise ValueError(f"{name} holds {have} bytes from its first element, the call needs {need}")
+
+
+def _check_fused(rank_in, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H, flags,
+                 q_bytes=None, s_bytes=None, strides=None):
+    """Checks of the fused entry points' tensors against M, H and the flags.
+    strides: (ld_in, ld_residual, ld_out, ld_residual_out, ld_fp8) for the
+    strided form (rows may be padded), else None (contiguous [M][H])."""
+    if M < 0 or H < 1:
+        return  # the C ABI rejects these sizes itself
+    dt = _T_BY_CODE.get(flags & 3)
+    dev = residual.device if hasattr(residual, "device") else None
+
+    def span(ld):
+        return 0 if M == 0 else (M - 1) * ld + H
+
+    ld = strides or (H, H, H, H, H)
+    contig = strides is None
+    for r, x in enumerate(rank_in):
+        _check(x, f"rank_in[{r}]", dtype=dt, numel=span(ld[0]), contiguous=contig, device=dev)
+    _check(residual, "residual", dtype=dt, numel=span(ld[1]), contiguous=contig)
+    _check(weight, "weight", dtype=dt, numel=H, device=dev)
+    _check(out, "out", dtype=dt, numel=span(ld[2]), contiguous=contig, device=dev)
+    _check(residual_out, "residual_out", dtype=dt, numel=span(ld[3]), contiguous=contig, device=dev)
+    if flags & FP8 or q_bytes is not None:
+        qb = (M * H if q_bytes is None else q_bytes) if contig else (0 if M == 0 else (M - 1) * ld[4] + H)
+        sb = M * 4 if s_bytes is None else s_bytes
+        _check(fp8_out, "fp8_out", nbytes=qb, contiguous=contig, device=dev)
+        _check(fp8_scale, "fp8_scale", nbytes=sb, device=dev)
+
+
 def _stream_handle(stream) -> int | None:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -136,6 +190,7 @@ def arrms_fused_config(rank_in, residual, weight, out, residual_out, fp8_out=Non
     """arrms_fused with an explicit row-kernel launch shape (0 = automatic)."""
     if M is None or H is None:
         M, H = residual.shape[-2], residual.shape[-1]
+    _check_fused(rank_in, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H, flags)
     rc = arrms_fused_config_raw(rank_in, len(rank_in), residual, weight, out, residual_out, fp8_out,
                                 fp8_scale, M, H, eps, flags, ppt, tpr, rows_per_block, blocks,
                                 _stream_handle(stream), load_window=load_window)
@@ -152,6 +207,7 @@ def arrms_fused(rank_in, residual, weight, out, residual_out, fp8_out=None, fp8_
     """
     if M is None or H is None:
         M, H = residual.shape[-2], residual.shape[-1]
+    _check_fused(rank_in, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H, flags)
     st = _stream_handle(stream)
     rc = arrms_fused_raw(rank_in, len(rank_in), residual, weight, out, residual_out, fp8_out,
                          fp8_scale, M, H, eps, flags, st)
@@ -196,6 +252,8 @@ def arrms_fused_strided(rank_in, residual, weight, out, residual_out, fp8_out=No
     ld_out = _row_stride(out, H) if ld_out is None else ld_out
     ld_residual_out = _row_stride(residual_out, H) if ld_residual_out is None else ld_residual_out
     ld_fp8 = _row_stride(fp8_out, H) if ld_fp8 is None else ld_fp8
+    _check_fused(rank_in, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H, flags,
+                 strides=(ld_in, ld_residual, ld_out, ld_residual_out, ld_fp8))
     rc = arrms_fused_strided_raw(rank_in, len(rank_in), residual, weight, out, residual_out, fp8_out,
                                  fp8_scale, M, H, ld_in, ld_residual, ld_out, ld_residual_out, ld_fp8,
                                  eps, flags, _stream_handle(stream))
@@ -219,6 +277,14 @@ def arrms_fused_quant(rank_in, residual, weight, out, residual_out, q_out, q_sca
     or QUANT_MXFP4); ``out`` is the optional T mirror."""
     if M is None or H is None:
         M, H = residual.shape[-2], residual.shape[-1]
+    if quant == QUANT_FP8_GROUP:
+        qb, sb = M * H, M * (H // FP8_GROUP_SIZE) * 4
+    elif quant == QUANT_MXFP4:
+        qb, sb = M * H // 2, M * (H // MX_BLOCK)
+    else:
+        qb, sb = M * H, M * 4
+    _check_fused(rank_in, residual, weight, out, residual_out, q_out, q_scale, M, H, flags,
+                 q_bytes=qb, s_bytes=sb)
     rc = arrms_fused_quant_raw(rank_in, len(rank_in), residual, weight, out, residual_out, q_out, q_scale,
                                M, H, eps, flags, quant, _stream_handle(stream))
     if rc != OK:
@@ -236,6 +302,11 @@ def arrms_allreduce_sum(rank_in, out, *, flags: int, n: int | None = None, strea
     (contiguous tensors of n elements; n defaults to out.numel())."""
     if n is None:
         n = out.numel()
+    dt = _T_BY_CODE.get(flags & 3) if not (flags & ~3) else None
+    dev = out.device if hasattr(out, "device") else None
+    for r, x in enumerate(rank_in):
+        _check(x, f"rank_in[{r}]", dtype=dt, numel=n, device=dev)
+    _check(out, "out", dtype=dt, numel=n)
     rc = arrms_allreduce_sum_raw(rank_in, len(rank_in), out, n, flags, _stream_handle(stream))
     if rc != OK:
         raise ArrmsError(rc, "arrms_allreduce_sum")

@@ -14,7 +14,9 @@
 #include <mutex>
 
 #include "arrms.h"
+#include "arrms_tuning.h"
 #include "launch.hpp"
+#include "staging.hpp"
 
 namespace {
 
@@ -212,8 +214,11 @@ int choose_path(int M, int H, int R, int flags)
 // rows of 513 to 1024 packs take one pack per thread (blocks of up to 1024
 // threads), and the FP8 epilogue, with more per-element work after the row
 // reduction, caps PPT at 3.
-arrms::RowShape choose_shape(int P, int R, long long M, bool fp8)
+arrms::RowShape choose_shape(int P, int R, long long M, bool fp8, bool fp32)
 {
+    // fp32 kernels take blocks of up to 1024 threads at any PPT (rows of up to
+    // 4096 packs); the others at one pack per thread only
+    const int wide_block = fp32 ? 1024 : 512;
     arrms::RowShape best = {0, 0, 0, false, 0, 0};
     long long best_key = -1;
     int cap = fp8 ? 3 : 4;
@@ -234,7 +239,7 @@ arrms::RowShape choose_shape(int P, int R, long long M, bool fp8)
             continue;
         int tpr = (P + ppt - 1) / ppt;
         tpr = (tpr + 63) / 64 * 64;
-        if (tpr > (cap == 1 ? 1024 : 512))  // one pack per thread: blocks of up to 1024
+        if (tpr > (cap == 1 ? 1024 : wide_block))  // one pack per thread: blocks of up to 1024
             continue;
         const int waste = tpr * ppt - P;
         const long long key = (long long)waste * 16 + (4 - ppt);
@@ -248,7 +253,7 @@ arrms::RowShape choose_shape(int P, int R, long long M, bool fp8)
         for (int c = 0; c < 4 && best.ppt == 0; ++c) {
             int tpr = (P + ppts[c] - 1) / ppts[c];
             tpr = (tpr + 63) / 64 * 64;
-            if (tpr <= 512)
+            if (tpr <= wide_block)
                 best = {ppts[c], tpr, 1, tpr * ppts[c] != P, 0, 0};
         }
     }
@@ -292,33 +297,40 @@ hipError_t launch_flat(int dt, const arrms::FlatArgs &a, int R, hipStream_t st)
     }
 }
 
-// ---- staging buffer: one per device, owned by the library ----------------
-struct Staging {
-    void *ptr;
-    size_t bytes;
-};
+// ---- staging buffers: one per device, owned by the library (staging.hpp) ----
+int staging_alloc(void **p, size_t bytes)
+{
+    if (hipMalloc(p, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return -1;
+    }
+    return 0;
+}
+
+int staging_wait(void)
+{
+    if (hipDeviceSynchronize() != hipSuccess) {
+        (void)hipGetLastError();
+        return -1;
+    }
+    return 0;
+}
+
+int staging_free(void *p)
+{
+    if (hipFree(p) != hipSuccess) {
+        (void)hipGetLastError();
+        return -1;
+    }
+    return 0;
+}
+
 std::mutex g_staging_mu;
-Staging g_staging[kMaxDevices];
+arrms::StagingPool<kMaxDevices> g_staging({staging_alloc, staging_wait, staging_free});
 
 int reserve_locked(int dev, size_t bytes)
 {
-    if (g_staging[dev].bytes >= bytes && g_staging[dev].ptr)
-        return ARRMS_OK;
-    void *p = nullptr;
-    if (hipMalloc(&p, bytes) != hipSuccess) {
-        (void)hipGetLastError();
-        return ARRMS_ERR_HIP;
-    }
-    if (g_staging[dev].ptr) {
-        if (hipDeviceSynchronize() != hipSuccess || hipFree(g_staging[dev].ptr) != hipSuccess) {
-            (void)hipFree(p);
-            (void)hipGetLastError();
-            return ARRMS_ERR_HIP;
-        }
-    }
-    g_staging[dev].ptr = p;
-    g_staging[dev].bytes = bytes;
-    return ARRMS_OK;
+    return g_staging.reserve(dev, bytes) == 0 ? ARRMS_OK : ARRMS_ERR_HIP;
 }
 
 int current_device(int *dev)
@@ -376,15 +388,7 @@ int arrms_release_staging(void)
     if (rc != ARRMS_OK)
         return rc;
     std::lock_guard<std::mutex> lk(g_staging_mu);
-    if (!g_staging[dev].ptr)
-        return ARRMS_OK;
-    if (hipDeviceSynchronize() != hipSuccess || hipFree(g_staging[dev].ptr) != hipSuccess) {
-        (void)hipGetLastError();
-        return ARRMS_ERR_HIP;
-    }
-    g_staging[dev].ptr = nullptr;
-    g_staging[dev].bytes = 0;
-    return ARRMS_OK;
+    return g_staging.release(dev) == 0 ? ARRMS_OK : ARRMS_ERR_HIP;
 }
 
 size_t arrms_staging_bytes(void)
@@ -393,7 +397,7 @@ size_t arrms_staging_bytes(void)
     if (current_device(&dev) != ARRMS_OK)
         return 0;
     std::lock_guard<std::mutex> lk(g_staging_mu);
-    return g_staging[dev].ptr ? g_staging[dev].bytes : 0;
+    return g_staging.bytes(dev);
 }
 
 }  // extern "C"
@@ -406,7 +410,7 @@ struct ShapeReq {
 
 // Apply an explicit shape request on top of the automatic choice; returns
 // false when the request cannot cover a row of P packs.
-bool apply_shape(const ShapeReq *req, int P, int R, long long M, arrms::RowShape &s)
+bool apply_shape(const ShapeReq *req, int P, int R, long long M, bool fp32, arrms::RowShape &s)
 {
     (void)R;
     (void)M;
@@ -424,8 +428,8 @@ bool apply_shape(const ShapeReq *req, int P, int R, long long M, arrms::RowShape
             return false;
         s.tpr = req->tpr;
     }
-    // blocks of one pack per thread may hold 1024 threads, others 512
-    const int max_block = s.ppt == 1 ? 1024 : 512;
+    // blocks of one pack per thread or of fp32 rows may hold 1024 threads, others 512
+    const int max_block = (s.ppt == 1 || fp32) ? 1024 : 512;
     if ((long long)s.tpr * s.ppt < P || s.tpr > max_block)
         return false;
     s.tail = s.tpr * s.ppt != P;
@@ -485,8 +489,8 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
         for (int r = 0; r < R; ++r)
             a.in[r] = rank_in[r];
         a.M = M;
-        arrms::RowShape s = choose_shape(P, R, M, fp8);
-        if (s.ppt == 0 || !apply_shape(req, P, R, M, s))
+        arrms::RowShape s = choose_shape(P, R, M, fp8, dt == DT_FP32);
+        if (s.ppt == 0 || !apply_shape(req, P, R, M, dt == DT_FP32, s))
             return ARRMS_ERR_UNSUPPORTED;
         a.tpr = s.tpr;
         return launch_row(dt, quant, out != nullptr, a, R, s, stream) == hipSuccess ? ARRMS_OK : ARRMS_ERR_HIP;
@@ -502,7 +506,7 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
     size_t staging_bytes;
     {
         std::lock_guard<std::mutex> lk(g_staging_mu);
-        if (!g_staging[dev].ptr) {
+        if (!g_staging.ptr(dev)) {
             hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
             if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
                 (void)hipGetLastError();
@@ -514,8 +518,8 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
             if (rc != ARRMS_OK)
                 return rc;
         }
-        staging = g_staging[dev].ptr;
-        staging_bytes = g_staging[dev].bytes;
+        staging = g_staging.ptr(dev);
+        staging_bytes = g_staging.bytes(dev);
     }
     const size_t row_bytes = (size_t)H * (size_t)e;
     const long long cap = (long long)(staging_bytes / row_bytes);  // rows the staging holds
@@ -561,8 +565,8 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
         b.M = n;
         // the row pass takes the one-stage shape of the whole launch, so both paths
         // reduce the row statistics in the same order and give the same bits
-        arrms::RowShape s = choose_shape(P, R, M, fp8);
-        if (s.ppt == 0 || !apply_shape(req, P, R, n, s))
+        arrms::RowShape s = choose_shape(P, R, M, fp8, dt == DT_FP32);
+        if (s.ppt == 0 || !apply_shape(req, P, R, n, dt == DT_FP32, s))
             return ARRMS_ERR_UNSUPPORTED;
         b.tpr = s.tpr;
         if (launch_row(dt, quant, out != nullptr, b, 1, s, stream) != hipSuccess)

@@ -295,12 +295,6 @@ ARRMS_DEV void bstore4(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t off)
 // FP8 epilogue on 2800 x 6144 fp16 rows, but with residual_out after the
 // codes (as now) the wide window is 0.1 us faster still; it was 0.2 us slower
 // for per-group FP8 and equal for MXFP4 and for 18-load bf16 rows.
-#ifndef ARRMS_ROUT_LATE_ALL
-#define ARRMS_ROUT_LATE_ALL 0
-#endif
-#ifndef ARRMS_LATE_WEIGHTS
-#define ARRMS_LATE_WEIGHTS 1
-#endif
 // The narrow window: 2 loads per thread; 3 for the two-stage row pass (R = 1).
 // Measured on 1024 x 6144 rows with residual_out written after the T output:
 // R = 4 14.34 -> 14.13-14.15 us from 3 to 2 (4: 14.33-14.35), R = 3 12.40 ->
@@ -562,7 +556,7 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
     // waiting, so it writes residual_out pack by pack in phase 1.
     constexpr bool mid_ranks = R >= 2 && R <= 6;
     constexpr bool quant_out = FP8 || GROUPQ;
-    constexpr bool rout_late = W < NL || ARRMS_ROUT_LATE_ALL || (quant_out && mid_ranks);
+    constexpr bool rout_late = W < NL || (quant_out && mid_ranks);
     constexpr bool rout_after_y = rout_late && (EPI == EPI_T || quant_out) && mid_ranks;
     // w_eff = w + gadd: 1 under gemma_norm, else -0.0, which adds nothing to
     // any value (signed zeros included), so one fp64 add serves both modes
@@ -591,11 +585,6 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
         // registers through phase 1 nor sit in the load window.
         const __amdgpu_buffer_rsrc_t rw = row_rsrc(a.weight, 0, 0, rb);
         u32x4 w[PPT];
-        if constexpr (!ARRMS_LATE_WEIGHTS) {
-#pragma unroll
-            for (int k = 0; k < PPT; ++k)
-                w[k] = bload_cached(rw, (uint32_t)(c.lt + k * c.tpr) * 16u);
-        }
         const long long row = g * c.rpb + c.slot;
         __amdgpu_buffer_rsrc_t sin[NS];
         in_streams<R>(a, row, rb, sin);
@@ -620,12 +609,10 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
                     x[kk][r] = bload(sin[r], (uint32_t)(c.lt + kk * c.tpr) * 16u);  // kk < PPT here
                     wait_vm<W - 1>();
                 }
-                if constexpr (ARRMS_LATE_WEIGHTS) {
-                    if (i == NL - 1) {
+                if (i == NL - 1) {
 #pragma unroll
-                        for (int k = 0; k < PPT; ++k)
-                            w[k] = bload_cached(rw, (uint32_t)(c.lt + k * c.tpr) * 16u);
-                    }
+                    for (int k = 0; k < PPT; ++k)
+                        w[k] = bload_cached(rw, (uint32_t)(c.lt + k * c.tpr) * 16u);
                 }
                 const int j = i - (W - 1);
                 if (j >= 0 && j % NS == NS - 1) {
@@ -823,9 +810,12 @@ ARRMS_DEV void row_loop(const RowArgs &a, const RowCtx &c, double (&red)[2][kMax
 }
 
 // Blocks of up to 1024 threads for one pack per thread (a whole wide row per
-// block), 512 otherwise (more packs per thread hold more registers).
+// block) and for fp32 rows (up to 16384 elements = 4096 packs: 1024 threads x
+// 4 packs), 512 otherwise (more packs per thread hold more registers).
+template <int DT, int PPT> constexpr int row_max_block() { return (PPT == 1 || DT == DT_FP32) ? 1024 : 512; }
+
 template <int DT, int R, int PPT, int EPI, int WIN>
-__global__ void __launch_bounds__(PPT == 1 ? 1024 : 512) row_kernel(const RowArgs a)
+__global__ void __launch_bounds__((row_max_block<DT, PPT>())) row_kernel(const RowArgs a)
 {
     RowCtx c;
     const int tid = threadIdx.x;
@@ -1003,7 +993,7 @@ static hipError_t row_go(const RowArgs &a, const RowShape &s, hipStream_t st)
     const int block = s.tpr * s.rpb;
     const long long groups = (a.M + s.rpb - 1) / s.rpb;
     const long long grid = (s.grid > 0 && s.grid < groups) ? s.grid : groups;
-    if (grid > 0x7fffffffLL || block > (PPT == 1 ? 1024 : 512) || s.tpr != a.tpr)
+    if (grid > 0x7fffffffLL || block > row_max_block<DT, PPT>() || s.tpr != a.tpr)
         return hipErrorInvalidValue;
     RowArgs b = a;
     b.rpb = s.rpb;

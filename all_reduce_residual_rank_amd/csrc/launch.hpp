@@ -67,15 +67,9 @@ struct RowShape {
     int window;
 };
 
-#ifndef ARRMS_FLAT_PPT
-#define ARRMS_FLAT_PPT 2
-#endif
-#ifndef ARRMS_FLAT_WINDOW
-#define ARRMS_FLAT_WINDOW 2
-#endif
 constexpr int kFlatThreads = 256;
-constexpr int kFlatPacksPerThread = ARRMS_FLAT_PPT;
-constexpr int kFlatWindow = ARRMS_FLAT_WINDOW;  // 16-byte loads in flight per thread
+constexpr int kFlatPacksPerThread = 2;
+constexpr int kFlatWindow = 2;  // 16-byte loads in flight per thread
 constexpr int kFlatTile = kFlatThreads * kFlatPacksPerThread;
 
 // Row kernels, one entry per dtype and epilogue (kern_<dtype>_<epilogue>.hip):

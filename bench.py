@@ -7,11 +7,29 @@ rotating buffer sets (>= 512 MiB in total, twice the 256 MB Infinity Cache) that
 every call reads cold data from HBM. Calls are captured in a HIP graph and
 timed with HIP events on the stream the kernels run on.
 
+Timing protocol (every figure below):
+  pre-roll    the timed graph itself is replayed, untimed, until at least
+              PREROLL_CALLS calls and PREROLL_SECONDS have run: the per-call time
+              of a fresh process keeps falling over its first few hundred calls
+              while clocks and memory settle (reported as preroll_calls);
+  warm-up     then --warmup further calls, untimed;
+  timed       exactly --steps calls: one replay of the graph between two HIP
+              events. The replay is queued behind a short GPU spin and one
+              untimed lead-in replay, so the host's graph-launch latency never
+              falls between the events: the figure is the GPU time of back-to-
+              back calls. Further replays, queued the same way, give the spread.
+
 Prints one JSON line:
   value       achieved GB/s by the metric's byte count (R+2)*M*H*2 + H*2
   roofline    algorithmic bytes per launch ((R+3)*M*H*e + H*e: R inputs and the
               residual read, out and residual_out written, the weight) over the
               measured kernel duration, against MI355X's 8 TB/s HBM peak
+  probe       a data-movement-only kernel over the same bytes (5 read and 2 write
+              streams per row, no arithmetic), the measured ceiling the fused
+              kernel is compared with (frac_of_probe)
+  workloads   every workload of the scope table (the 16-row decode case, the
+              headline on both paths, the FP8 workload, the R=8 wide rows on both
+              paths, the tail/decode sweep) with us/call per path
   cpu_baseline  the CPU oracle, single-threaded, on the same workload
   quant_epilogues  per-token FP8, per-group FP8 and MXFP4 outputs on the FP8
               workload's rows (R=4, 2800 x 6144 fp16, gemma_norm)
@@ -24,6 +42,7 @@ Prints one JSON line:
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -38,15 +57,18 @@ if ROOT not in sys.path:
 METRIC = "µs/call and achieved HBM GB/s (% of peak) for fused sum+RMSNorm, R=4, H=6144"
 PEAK_GBS = 8000.0
 ROTATE_BYTES = 512 << 20
+PREROLL_CALLS = 4096
+PREROLL_SECONDS = 0.5
+MAX_GRAPH_CALLS = 4096       # small workloads: more calls per graph, so that more distinct data is touched
+BANDWIDTH_BOUND_BYTES = 32 << 20   # per call: below this a launch is latency-bound (report us only)
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=256)
-    p.add_argument("--warmup", type=int, default=4096,
-                   help="untimed calls first: the per-call time keeps falling over the first ~500 "
-                        "calls (clocks and memory settling), so warm up well past that")
+    p.add_argument("--warmup", type=int, default=256,
+                   help="untimed calls after the pre-roll (which always runs first)")
     p.add_argument("--workload", default="r4_m1024_h6144_bf16_rowscale")
     p.add_argument("--path", choices=("auto", "one", "two"), default="auto")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -61,10 +83,15 @@ def parse():
                    help="skip the plain 256 MiB device copy timed for reference")
     p.add_argument("--no-quant", action="store_true",
                    help="skip the per-token / per-group FP8 / MXFP4 epilogue timings")
+    p.add_argument("--no-workloads", action="store_true",
+                   help="skip the other workloads of the scope table")
+    p.add_argument("--no-probe", action="store_true", help="skip the data-movement probe")
     p.add_argument("--replays", type=int, default=20,
                    help="further timed replays of the chosen path, for median/min (0: none)")
     p.add_argument("--sum-only", action="store_true",
                    help="time only the plain rank all-reduce (R=4, 1024 x 6144 bf16 message)")
+    p.add_argument("--probe-only", action="store_true",
+                   help="time only the data-movement probe of the chosen workload")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 256 MiB device-to-device copy (4 times) so that a "
                         "profiler's FETCH_SIZE/WRITE_SIZE can be scaled by a kernel of known size")
@@ -78,6 +105,22 @@ def sources_digest() -> str:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
+
+
+def file_sha256(path: str) -> str | None:
+    try:
+        with open(path, "rb") as f:
+            return hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+
+
+def rocm_version() -> str | None:
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            return f.read().strip()
+    except OSError:
+        return None
 
 
 def load_traffic(workload: str, path: str, digest: str):
@@ -96,17 +139,136 @@ def load_traffic(workload: str, path: str, digest: str):
     return e.get("hbm_bytes_per_launch")
 
 
+# ---- timing ----------------------------------------------------------------
+
+_SPIN_CYCLES_PER_US = None
+
+
+def _spin_rate(torch):
+    """Cycles of torch.cuda._sleep per microsecond on this GPU (measured once)."""
+    global _SPIN_CYCLES_PER_US
+    if _SPIN_CYCLES_PER_US is None:
+        cyc = 1 << 20
+        torch.cuda._sleep(cyc)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(cyc)
+        e1.record()
+        torch.cuda.synchronize()
+        _SPIN_CYCLES_PER_US = cyc / max(e0.elapsed_time(e1) * 1000.0, 1.0)
+    return _SPIN_CYCLES_PER_US
+
+
+class Graph:
+    """`ncalls` calls (cycling through `calls`) captured in one HIP graph on a
+    side stream."""
+
+    def __init__(self, torch, calls, ncalls):
+        self.torch = torch
+        self.ncalls = ncalls
+        self.s = torch.cuda.Stream()
+        self.s.wait_stream(torch.cuda.current_stream())
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g, stream=self.s):
+            for i in range(ncalls):
+                calls[i % len(calls)](self.s)
+        torch.cuda.synchronize()
+        self.host_launch_s = None
+
+    def replay(self, n=1):
+        with self.torch.cuda.stream(self.s):
+            for _ in range(n):
+                self.g.replay()
+
+    def preroll(self, min_calls=PREROLL_CALLS, min_seconds=PREROLL_SECONDS):
+        """Untimed replays until at least min_calls calls and min_seconds have run;
+        returns the number of calls. Also measures the host's launch time of one
+        replay (for the spin that keeps it out of the timed region)."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        done = 0
+        launch = []
+        batch = max(1, 64 // self.ncalls)
+        while done < min_calls or time.perf_counter() - t0 < min_seconds:
+            for _ in range(batch):
+                h0 = time.perf_counter()
+                self.replay()
+                launch.append(time.perf_counter() - h0)
+                done += self.ncalls
+            torch.cuda.synchronize()
+        self.host_launch_s = statistics.median(launch)
+        return done
+
+    def timed(self, nrep):
+        """Times nrep back-to-back replays between HIP events: a GPU spin long
+        enough for the host to queue everything, one untimed lead-in replay,
+        then the timed replays. Returns the ms of each."""
+        torch = self.torch
+        if self.host_launch_s is None:
+            h0 = time.perf_counter()
+            self.replay()
+            self.host_launch_s = time.perf_counter() - h0
+        spin_us = 200.0 + 3.0 * (nrep + 1) * self.host_launch_s * 1e6
+        cycles = int(spin_us * _spin_rate(torch))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(nrep + 1)]
+        torch.cuda.synchronize()
+        with torch.cuda.stream(self.s):
+            torch.cuda._sleep(cycles)
+            self.g.replay()              # lead-in, untimed
+            ev[0].record(self.s)
+            for i in range(nrep):
+                self.g.replay()
+                ev[i + 1].record(self.s)
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) for i in range(nrep)]
+
+
+def time_calls(torch, calls, steps, warmup, replays=0, ncalls=None):
+    """Pre-roll, warm up, then time exactly `steps` calls (one graph replay), and
+    `replays` further replays. Returns a dict with us per call of the timed
+    replay, the replays' spread and the pre-roll count."""
+    ncalls = steps if ncalls is None else ncalls
+    g = Graph(torch, calls, ncalls)
+    pre = g.preroll()
+    if warmup > 0:
+        if warmup % ncalls == 0:
+            g.replay(warmup // ncalls)
+        else:
+            gw = Graph(torch, calls, warmup)
+            gw.replay()
+            del gw
+    torch.cuda.synchronize()
+    ms = g.timed(1 + replays)
+    us = [m * 1000.0 / ncalls for m in ms]
+    out = {"us_per_call": us[0], "preroll_calls": pre, "calls_per_graph": ncalls,
+           "host_launch_us": round(g.host_launch_s * 1e6, 1)}
+    if replays:
+        r = sorted(us[1:])
+        out["replays"] = {"n": len(r), "median_us": round(statistics.median(r), 3), "min_us": round(r[0], 3),
+                          "max_us": round(r[-1], 3)}
+    del g
+    return out
+
+
+# ---- workloads ------------------------------------------------------------
+
 class Sets:
-    """Rotating device buffer sets of one workload."""
+    """Rotating device buffer sets of one workload (nsets copies of its inputs,
+    made on the device from one upload)."""
 
     def __init__(self, wl, nsets, torch):
         from all_reduce_residual_rank_amd import workloads as wlmod
         dev = torch.device("cuda")
         T = wlmod.DTYPES[wl.dtype]
         xs, res, w = wlmod.make_inputs(wl, seed=0)
+        xd = [x.to(dev) for x in xs]
+        rd, wd = res.to(dev), w.to(dev)
         self.sets = []
         for s in range(nsets):
-            d = {"xs": [x.to(dev) for x in xs], "res": res.to(dev), "w": w.to(dev),
+            d = {"xs": [x.clone() for x in xd], "res": rd.clone(), "w": wd,
                  "rout": torch.empty(wl.M, wl.H, dtype=T, device=dev),
                  "out": torch.empty(wl.M, wl.H, dtype=T, device=dev) if (wl.mirror or not wl.fp8) else None,
                  "q": torch.empty(wl.M, wl.H, dtype=torch.uint8, device=dev) if wl.fp8 else None,
@@ -119,60 +281,60 @@ def call(arrms, wl, d, flags, stream):
                       flags=flags, M=wl.M, H=wl.H, stream=stream)
 
 
-def time_graph(torch, calls, steps, warmup, extra=None):
-    """Warm up, then time exactly `steps` calls replayed from one HIP graph.
-    calls: functions f(stream) that each enqueue one call; used in turn.
-    extra: a list that receives the ms of further timed replays (len(extra)
-    given as a count in extra[0]), for the spread; the first timing is the
-    one returned."""
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    n = len(calls)
-    gk = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gk, stream=s):
-        for i in range(steps):
-            calls[i % n](s)
-    torch.cuda.synchronize()
-    if warmup > 0 and warmup % steps == 0:
-        # warm up with the timed graph itself (its first replays also carry the
-        # graph's one-time upload)
-        with torch.cuda.stream(s):
-            for _ in range(warmup // steps):
-                gk.replay()
-    elif warmup > 0:
-        gw = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gw, stream=s):
-            for i in range(warmup):
-                calls[i % n](s)
-        torch.cuda.synchronize()
-        with torch.cuda.stream(s):
-            gw.replay()
-        del gw
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(s):
-        e0.record(s)
-        gk.replay()
-        e1.record(s)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
-    if extra:
-        n = int(extra.pop())
-        for _ in range(n):
-            with torch.cuda.stream(s):
-                e0.record(s)
-                gk.replay()
-                e1.record(s)
-            torch.cuda.synchronize()
-            extra.append(e0.elapsed_time(e1))
-    del gk
-    return ms
+def algo_bytes_of(wl) -> int:
+    """Bytes one call must move: the R inputs and the residual read, residual_out
+    and the T output (or FP8 codes + scales, plus the optional mirror) written,
+    and the weight."""
+    e = wl.esize
+    n = wl.M * wl.H
+    if wl.fp8:
+        return (wl.R + 2) * n * e + wl.H * e + n + wl.M * 4 + (n * e if wl.mirror else 0)
+    return (wl.R + 3) * n * e + wl.H * e
 
 
-def time_path(torch, arrms, wl, sets, flags, steps, warmup, extra=None):
-    calls = [lambda st, d=d: call(arrms, wl, d, flags, st) for d in sets.sets]
-    return time_graph(torch, calls, steps, warmup, extra)
+def metric_bytes_of(wl) -> int:
+    return (wl.R + 2) * wl.M * wl.H * wl.esize + wl.H * wl.esize
+
+
+def nsets_for(wl, ncalls) -> int:
+    set_bytes = (wl.R + 3) * wl.M * wl.H * wl.esize
+    return max(2, min(ncalls, -(-ROTATE_BYTES // set_bytes)))
+
+
+def calls_for(wl, steps) -> int:
+    """Calls per graph for a workload timed beside the headline: at least `steps`,
+    and for small workloads enough to touch ROTATE_BYTES of distinct data (capped)."""
+    set_bytes = (wl.R + 3) * wl.M * wl.H * wl.esize
+    return max(steps, min(MAX_GRAPH_CALLS, -(-ROTATE_BYTES // set_bytes)))
+
+
+def time_workload(torch, arrms, wl, paths, steps, warmup, sets=None):
+    """us/call of a workload on each of `paths` over rotating buffer sets."""
+    ncalls = calls_for(wl, steps)
+    own = sets is None
+    if own:
+        sets = Sets(wl, nsets_for(wl, ncalls), torch)
+    res = {"R": wl.R, "M": wl.M, "H": wl.H, "dtype": wl.dtype, "gemma": wl.gemma, "fp8": wl.fp8,
+           "calls_per_graph": ncalls,
+           "footprint_bytes": min(ncalls, len(sets.sets)) * algo_bytes_of(wl),
+           "metric_bytes": metric_bytes_of(wl), "algorithmic_bytes": algo_bytes_of(wl)}
+    bw = algo_bytes_of(wl) >= BANDWIDTH_BOUND_BYTES
+    pf = {"one": arrms.FORCE_ONE_STAGE, "two": arrms.FORCE_TWO_STAGE}
+    for p in paths:
+        calls = [lambda st, d=d: call(arrms, wl, d, wl.flags | pf[p], st) for d in sets.sets]
+        t = time_calls(torch, calls, steps, warmup, ncalls=ncalls)
+        us = t["us_per_call"]
+        r = {"us_per_call": round(us, 3)}
+        if bw:
+            r["metric_gbs"] = round(metric_bytes_of(wl) / (us * 1e-6) / 1e9, 1)
+            r["achieved_gbs"] = round(algo_bytes_of(wl) / (us * 1e-6) / 1e9, 1)
+            r["frac"] = round(algo_bytes_of(wl) / (us * 1e-6) / 1e9 / PEAK_GBS, 4)
+        res[p] = r
+    res["bound"] = "hbm" if bw else "latency"
+    if own:
+        del sets
+        torch.cuda.empty_cache()
+    return res
 
 
 def copy_reference(torch, nbytes=256 << 20, reps=10):
@@ -222,9 +384,9 @@ def time_strided(torch, arrms, wl, pad, steps, warmup):
                                   flags=wl.flags | arrms.FORCE_ONE_STAGE, stream=st)
 
     calls = [lambda st, d=d: one(d, st) for d in sets]
-    ms = time_graph(torch, calls, steps, warmup)
+    t = time_calls(torch, calls, steps, warmup)
     del sets
-    return ms * 1000.0 / steps
+    return t["us_per_call"]
 
 
 def time_quant(torch, arrms, wl, quant, steps, warmup):
@@ -244,7 +406,9 @@ def time_quant(torch, arrms, wl, quant, steps, warmup):
     algo = (wl.R + 2) * M * H * e + H * e + qbytes + sbytes
     xs, res, w = wlmod.make_inputs(wl, seed=0)
     nsets = max(2, -(-ROTATE_BYTES // algo))
-    sets = [{"xs": [x.to(dev) for x in xs], "res": res.to(dev), "w": w.to(dev),
+    xd = [x.to(dev) for x in xs]
+    rd = res.to(dev)
+    sets = [{"xs": [x.clone() for x in xd], "res": rd.clone(), "w": w.to(dev),
              "rout": torch.empty(M, H, dtype=T, device=dev),
              "q": torch.empty(qbytes, dtype=torch.uint8, device=dev),
              "s": torch.empty(sbytes, dtype=torch.uint8, device=dev)} for _ in range(nsets)]
@@ -254,9 +418,9 @@ def time_quant(torch, arrms, wl, quant, steps, warmup):
         arrms.arrms_fused_quant(d["xs"], d["res"], d["w"], None, d["rout"], d["q"], d["s"], eps=wl.eps,
                                 flags=flags, quant=quant, M=M, H=H, stream=st)
 
-    ms = time_graph(torch, [lambda st, d=d: one(d, st) for d in sets], steps, warmup)
+    t = time_calls(torch, [lambda st, d=d: one(d, st) for d in sets], steps, warmup)
     del sets
-    return ms * 1000.0 / steps, algo
+    return t["us_per_call"], algo
 
 
 def time_sum(torch, arrms, case, R, steps, warmup):
@@ -266,36 +430,65 @@ def time_sum(torch, arrms, case, R, steps, warmup):
     dev = torch.device("cuda")
     xs = wlmod.make_sum_inputs(R, case.numel, 0, case.dtype)
     nsets = max(2, -(-ROTATE_BYTES // ((R + 1) * case.nbytes)))
-    sets = [([x.to(dev) for x in xs], torch.empty(case.numel, dtype=wlmod.DTYPES[case.dtype], device=dev))
+    xd = [x.to(dev) for x in xs]
+    sets = [([x.clone() for x in xd], torch.empty(case.numel, dtype=wlmod.DTYPES[case.dtype], device=dev))
             for _ in range(nsets)]
     flags = wlmod.DT_CODE[case.dtype]
     calls = [lambda st, d=d: arrms.arrms_allreduce_sum(d[0], d[1], flags=flags, stream=st) for d in sets]
-    ms = time_graph(torch, calls, steps, warmup)
+    t = time_calls(torch, calls, steps, warmup)
     del sets
-    return ms * 1000.0 / steps, (R + 1) * case.nbytes
+    return t["us_per_call"], (R + 1) * case.nbytes
 
 
 def time_hot(torch, arrms, wl, sets, flags, reps=64):
     """Single buffer set replayed: cache-resident ("hot") context number."""
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=s):
-        for _ in range(reps):
-            call(arrms, wl, sets.sets[0], flags, s)
-    torch.cuda.synchronize()
-    res = []
-    for _ in range(5):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(s):
-            e0.record(s)
-            g.replay()
-            e1.record(s)
-        torch.cuda.synchronize()
-        res.append(e0.elapsed_time(e1) * 1000.0 / reps)
-    return min(res)
+    g = Graph(torch, [lambda st: call(arrms, wl, sets.sets[0], flags, st)], reps)
+    g.preroll(min_calls=reps * 8, min_seconds=0.0)
+    ms = g.timed(5)
+    del g
+    return min(ms) * 1000.0 / reps
 
+
+# ---- the data-movement probe (measured ceiling) ---------------------------
+
+def load_probe():
+    """The streaming probe library (probe/libstream_probe.so), or None."""
+    path = os.path.join(ROOT, "probe", "libstream_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    lib.probe_rows.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.POINTER(vp), ctypes.c_int,
+                               ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    lib.probe_rows.restype = ctypes.c_int
+    return lib
+
+
+def time_probe(torch, lib, wl, sets, steps, warmup, replays):
+    """The probe over the workload's own rotating buffers: every row's R + 1 input
+    streams read and two output streams written (residual_out and out), in the
+    fused kernel's launch shape and load window, with no arithmetic."""
+    from all_reduce_residual_rank_amd import arrms
+    P = wl.H * wl.esize // 16
+    ppt = 4 if P % 4 == 0 and P // 4 <= 512 else 2
+    tpr = -(-P // ppt)
+    tpr = -(-tpr // 64) * 64
+    vp = ctypes.c_void_p
+
+    def one(d, st):
+        ins = (vp * (wl.R + 1))(*[x.data_ptr() for x in d["xs"]], d["res"].data_ptr())
+        outs = (vp * 2)(d["rout"].data_ptr(), d["out"].data_ptr())
+        rc = lib.probe_rows(ins, wl.R + 1, outs, 2, wl.M, wl.H * wl.esize, ppt, tpr, 2, st.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"probe_rows failed: {rc}")
+
+    calls = [lambda st, d=d: one(d, st) for d in sets.sets]
+    t = time_calls(torch, calls, steps, warmup, replays=replays)
+    t["launch"] = {"packs_per_thread": ppt, "threads_per_row": tpr, "load_window": 2}
+    return t
+
+
+# ---- host facts -----------------------------------------------------------
 
 def read_clocks(torch):
     """Current shader and memory clocks of device 0, read from the amdgpu
@@ -334,6 +527,7 @@ def cpu_baseline(wl, budget_s):
 
     xb = [bits(x) for x in xs]
     rb, wb = bits(res), bits(w)
+
     def once(n):
         t0 = time.perf_counter()
         oracle.fused(xb, rb, wb, wl.eps, wl.flags & 0xF, rows=(0, n))
@@ -354,7 +548,8 @@ def cpu_baseline(wl, budget_s):
                      f"median of {len(times)} runs, {t * 1e3:.1f} ms each",
            "us_per_row": round(t / rows * 1e6, 3)}
     # the same sample split by rows over the host's cores (the oracle's C code
-    # runs outside the GIL), for context
+    # runs outside the GIL), for context: every core of the process's affinity
+    # mask, at most 16 (the CPU share of one GPU on the GPU machine)
     from concurrent.futures import ThreadPoolExecutor
     n = max(1, min(len(os.sched_getaffinity(0)), 16, rows))
     bounds = [(rows * i // n, rows * (i + 1) // n) for i in range(n)]
@@ -370,6 +565,7 @@ def cpu_baseline(wl, budget_s):
             tt.append(time.perf_counter() - t0)
     tm = statistics.median(tt)
     out["threads"] = {"value": round(metric_bytes / tm / 1e9, 4), "cores": n,
+                      "affinity_cores": len(os.sched_getaffinity(0)),
                       "sample": f"the same rows split over {n} threads, median of 3 runs, {tm * 1e3:.1f} ms each"}
     out["cpu_model"] = cpu_model()
     return out
@@ -385,6 +581,11 @@ def cpu_model():
     except OSError:
         pass
     return None
+
+
+def run_meta(torch, arrms):
+    return {"rocm": rocm_version(), "torch_hip": getattr(torch.version, "hip", None),
+            "libarrms_sha256": file_sha256(arrms.LIB_PATH), "sources_digest": sources_digest()}
 
 
 def main():
@@ -406,11 +607,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    digest = sources_digest()
     if args.sum_only:
         case = wlmod.SUM_HEADLINE
         us, nbytes = time_sum(torch, arrms, case, 4, args.steps, args.warmup)
         gbs = nbytes / (us * 1e-6) / 1e9
-        digest = sources_digest()
         print(json.dumps({
             "metric": "µs/call and achieved HBM GB/s of the plain rank all-reduce, R=4",
             "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -425,24 +626,26 @@ def main():
             "sources_digest": digest}), flush=True)
         return
     e = wl.esize
-    set_bytes = (wl.R + 3) * wl.M * wl.H * e
-    nsets = max(2, -(-ROTATE_BYTES // set_bytes))
-    sets = Sets(wl, nsets, torch)
+    ncalls = args.steps
+    sets = Sets(wl, nsets_for(wl, ncalls), torch)
+    if args.probe_only:
+        lib = load_probe()
+        if lib is None:
+            raise SystemExit("probe/libstream_probe.so is not built (python __graft_entry__.py)")
+        t = time_probe(torch, lib, wl, sets, args.steps, args.warmup, args.replays)
+        print(json.dumps({"probe": wl.name, **t}), flush=True)
+        return
     arrms.arrms_reserve_staging(0)
 
     path_flags = {"one": arrms.FORCE_ONE_STAGE, "two": arrms.FORCE_TWO_STAGE, "auto": 0}
     auto_path = {arrms.PATH_ONE_STAGE: "one", arrms.PATH_TWO_STAGE: "two"}[
         arrms.arrms_query_path(wl.M, wl.H, wl.R, wl.flags)]
     chosen = auto_path if args.path == "auto" else args.path
-    reps = [float(args.replays)]
-    ms = time_path(torch, arrms, wl, sets, wl.flags | path_flags[chosen], args.steps, args.warmup, reps)
-    us = ms * 1000.0 / args.steps
-    rep_us = sorted(r * 1000.0 / args.steps for r in reps)
-    metric_bytes = (wl.R + 2) * wl.M * wl.H * e + wl.H * e
-    algo_bytes = (wl.R + 3) * wl.M * wl.H * e + wl.H * e
-    if wl.fp8:
-        algo_bytes = (wl.R + 1) * wl.M * wl.H * e + wl.H * e + wl.M * wl.H + wl.M * 4 + \
-            (wl.M * wl.H * e if wl.mirror else 0) + wl.M * wl.H * e
+    calls = [lambda st, d=d: call(arrms, wl, d, wl.flags | path_flags[chosen], st) for d in sets.sets]
+    t = time_calls(torch, calls, args.steps, args.warmup, replays=args.replays, ncalls=ncalls)
+    us = t["us_per_call"]
+    metric_bytes = metric_bytes_of(wl)
+    algo_bytes = algo_bytes_of(wl)
     gbs = metric_bytes / (us * 1e-6) / 1e9
     achieved = algo_bytes / (us * 1e-6) / 1e9
 
@@ -451,33 +654,53 @@ def main():
         if p == chosen:
             other[p] = round(us, 3)
         elif not args.no_other_path:
-            ms2 = time_path(torch, arrms, wl, sets, wl.flags | path_flags[p], args.steps, args.warmup)
-            other[p] = round(ms2 * 1000.0 / args.steps, 3)
+            c2 = [lambda st, d=d: call(arrms, wl, d, wl.flags | path_flags[p], st) for d in sets.sets]
+            other[p] = round(time_calls(torch, c2, args.steps, args.warmup, ncalls=ncalls)["us_per_call"], 3)
     hot = None if args.no_hot else time_hot(torch, arrms, wl, sets, wl.flags | path_flags[chosen])
-    digest = sources_digest()
     traffic = load_traffic(wl.name, chosen, digest)
 
     line = {
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms / args.steps, 6), "higher_is_better": True, "scaling": "weak",
+        "ms_per_step": round(us / 1000.0, 6), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "R": wl.R, "M": wl.M, "H": wl.H, "dtype": wl.dtype,
-                   "gemma": wl.gemma, "fp8": wl.fp8, "path": chosen, "rotating_sets": nsets,
+                   "gemma": wl.gemma, "fp8": wl.fp8, "path": chosen, "rotating_sets": len(sets.sets),
                    "compute": "fp32 rank sums, fp64 row statistics"},
         "us_per_call": round(us, 3), "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
         "metric_bytes": metric_bytes,
+        "preroll_calls": t["preroll_calls"],
+        "timing": "HIP events around exactly `steps` back-to-back calls of one graph replay, queued behind a GPU "
+                  "spin and an untimed lead-in replay (no host launch gap inside); after the pre-roll and warm-up",
         "path_us": other, "hot_us_cache_resident": None if hot is None else round(hot, 3),
-        "replays": None if not rep_us else {"n": len(rep_us), "median_us": round(statistics.median(rep_us), 3),
-                                             "min_us": round(rep_us[0], 3), "max_us": round(rep_us[-1], 3)},
+        "replays": t.get("replays"),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": algo_bytes,
                      "kernel": "row_kernel" if chosen == "one" else "flat_kernel+row_kernel"},
-        "sources_digest": digest,
         "device": torch.cuda.get_device_name(0),
         "arch": torch.cuda.get_device_properties(0).gcnArchName,
+        **run_meta(torch, arrms),
     }
+    if not args.no_probe and not wl.fp8:
+        lib = load_probe()
+        if lib is not None:
+            pt = time_probe(torch, lib, wl, sets, args.steps, args.warmup, args.replays)
+            pu = pt["us_per_call"]
+            line["probe"] = {"kind": "data movement only: R+1 input and 2 output streams per row, no arithmetic",
+                             "us_per_call": round(pu, 3), "replays": pt.get("replays"),
+                             "achieved": round(algo_bytes / (pu * 1e-6) / 1e9, 2), **pt["launch"]}
+            line["probe_us"] = round(pu, 3)
+            line["frac_of_probe"] = round(pu / us, 4)
+    del sets
+    torch.cuda.empty_cache()
+    if not args.no_workloads:
+        wres = {}
+        for w2 in [wlmod.SMALL, wlmod.HEADLINE, wlmod.FP8_GEMMA, wlmod.WIDE_R8, *wlmod.TAILS, wlmod.TAIL_FP32]:
+            if w2.name == wl.name:
+                continue
+            wres[w2.name] = time_workload(torch, arrms, w2, ("one", "two"), args.steps, args.warmup)
+        line["workloads"] = wres
     if not args.no_sum:
         # the plain rank all-reduce (no norm) on the same rank inputs' size
         case = wlmod.SUM_HEADLINE

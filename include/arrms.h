@@ -48,8 +48,6 @@ extern "C" {
 #define ARRMS_FP8 8                /* per-token FP8 E4M3 output + fp32 per-row scales (PR #6699 Changes) */
 #define ARRMS_FORCE_ONE_STAGE 16   /* force the one-stage direct-read path */
 #define ARRMS_FORCE_TWO_STAGE 32   /* force the two-stage path (flat rank reduce into staging, then row pass) */
-#define ARRMS_EXACT_ONLY 64        /* verification: take the exact rounding branch for every element
-                                      (same results; used to check the fast branches bit for bit) */
 
 /* ---- quantised outputs of arrms_fused_quant ------------------------------- */
 #define ARRMS_QUANT_FP8_TOKEN 1    /* per-token FP8: as arrms_fused with ARRMS_FP8 */
@@ -61,7 +59,7 @@ extern "C" {
 /* ---- limits -------------------------------------------------------------- */
 #define ARRMS_MAX_RANKS 8          /* the pages go up to TP8 (PR #3462 Test Results) */
 #define ARRMS_MAX_HIDDEN 16384
-#define ARRMS_MAX_ROW_BYTES 32768 /* H * sizeof(T): a row is at most 2048 packs (fp32: H <= 8192) */
+#define ARRMS_MAX_ROW_BYTES 65536 /* H * sizeof(T): bf16/fp16 rows up to 32 KiB, fp32 up to 64 KiB */
 #define ARRMS_DEFAULT_STAGING_BYTES (16u << 20) /* 16 MiB staging region (PR #6699 Changes) */
 
 /* ---- paths returned by arrms_query_path ---------------------------------- */
@@ -104,8 +102,9 @@ extern "C" {
  * H            hidden size, 1 .. ARRMS_MAX_HIDDEN, with H * sizeof(T) % 16 == 0 and
  *              H * sizeof(T) <= ARRMS_MAX_ROW_BYTES.
  * eps          finite, >= 0.
- * flags        ARRMS_DTYPE_* | ARRMS_GEMMA | ARRMS_FP8 | at most one ARRMS_FORCE_* |
- *              ARRMS_EXACT_ONLY. ARRMS_FP8 requires bf16 or fp16.
+ * flags        ARRMS_DTYPE_* | ARRMS_GEMMA | ARRMS_FP8 | at most one ARRMS_FORCE_*
+ *              (and the verification bit of arrms_tuning.h). ARRMS_FP8 requires
+ *              bf16 or fp16.
  * stream       HIP stream; all work is enqueued on it, asynchronously.
  *
  * Every device pointer must be 16-byte aligned (fp8_scale: 4-byte aligned).
@@ -205,41 +204,24 @@ ARRMS_API int arrms_allreduce_sum(const void *const *rank_in, int R, void *out, 
                                   hipStream_t stream);
 
 /*
- * arrms_fused_config -- arrms_fused with an explicit launch shape for the row
- * kernel, for benchmarking and tuning (the automatic choice is the shape
- * arrms_fused takes). ppt: 16-byte packs per thread and row (1 to 4); tpr:
- * threads per row (a multiple of 64, tpr * ppt covering the row);
- * rows_per_block: rows handled side by side by one block (tpr *
- * rows_per_block at most 1024 threads with ppt = 1, else 512); blocks: the
- * number of blocks launched -- with fewer blocks than row groups each block
- * takes every blocks-th group of rows in turn; load_window: how many 16-byte
- * loads a thread keeps in flight -- 1 a narrow window (for large launches
- * whose rows are all resident at once), 2 a wide one (the whole row, up to a
- * cap: small launches, and large ones that run in several rounds of
- * blocks), 3 a medium one (8 loads; an alternative for the latter). 0 in any
- * of them keeps the automatic value; a negative value (or a load_window
- * above 3) gives ARRMS_ERR_INVALID and a shape that cannot cover a row
- * ARRMS_ERR_UNSUPPORTED. All other arguments, the results and the error
- * behaviour are arrms_fused's.
- */
-ARRMS_API int arrms_fused_config(const void *const *rank_in, int R, const void *residual,
-                                 const void *weight, void *out, void *residual_out, void *fp8_out,
-                                 float *fp8_scale, int M, int H, float eps, int flags, int ppt,
-                                 int tpr, int rows_per_block, int blocks, int load_window,
-                                 hipStream_t stream);
-
-/*
- * arrms_reserve_staging -- allocate the staging buffer of the two-stage path
- * on the current device, at least `bytes` (0: ARRMS_DEFAULT_STAGING_BYTES), the
+ * arrms_reserve_staging -- make the staging buffer of the two-stage path on
+ * the current device at least `bytes` (0: ARRMS_DEFAULT_STAGING_BYTES), the
  * per-rank staging region of PR #6699 Changes. A larger existing buffer is
- * kept. Call it before capturing a graph that may take the two-stage path.
- * Returns ARRMS_OK or ARRMS_ERR_HIP. Not to be called while work that uses the
- * buffer is in flight.
+ * kept. A smaller one is replaced by a new allocation and retired, not freed:
+ * two-stage work still in flight, and HIP graphs captured earlier (whose
+ * launches hold the old address), keep valid memory until
+ * arrms_release_staging. Call it before capturing a graph that may take the
+ * two-stage path. Returns ARRMS_OK or ARRMS_ERR_HIP (allocation failed;
+ * nothing changed).
  */
 ARRMS_API int arrms_reserve_staging(size_t bytes);
 
-/* arrms_release_staging -- free the current device's staging buffer (after
- * synchronising the device). Returns ARRMS_OK or ARRMS_ERR_HIP. */
+/* arrms_release_staging -- free the current device's staging buffer and every
+ * buffer retired by an earlier growth, after synchronising the device. Any HIP
+ * graph captured with a two-stage call on this device holds those addresses:
+ * destroy such graphs before calling it (a replay afterwards would touch freed
+ * memory). A later two-stage call reserves a new buffer. Returns ARRMS_OK or
+ * ARRMS_ERR_HIP. */
 ARRMS_API int arrms_release_staging(void);
 
 /* arrms_staging_bytes -- size of the current device's staging buffer (0 if none). */

@@ -109,7 +109,7 @@ static float bits_f32(uint32_t u)
 }
 
 /* bfloat16: 8 significant bits, the exponent range of binary32. */
-uint16_t orc_bf16_from_double(double v)
+static uint16_t orc_bf16_from_double(double v)
 {
     if (isnan(v))
         return (uint16_t)(signbit(v) ? 0xFFC0u : 0x7FC0u);
@@ -122,13 +122,13 @@ uint16_t orc_bf16_from_double(double v)
     return (uint16_t)(f32_bits((float)r) >> 16);
 }
 
-double orc_bf16_to_double(uint16_t b)
+static double orc_bf16_to_double(uint16_t b)
 {
     return (double)bits_f32((uint32_t)b << 16);
 }
 
 /* binary16: 11 significant bits, emin = -14, max 65504. */
-uint16_t orc_fp16_from_double(double v)
+static uint16_t orc_fp16_from_double(double v)
 {
     uint16_t sign = signbit(v) ? 0x8000u : 0;
     if (isnan(v))
@@ -147,7 +147,7 @@ uint16_t orc_fp16_from_double(double v)
     return (uint16_t)(sign | (uint16_t)((lead + 15) << 10) | mant);
 }
 
-double orc_fp16_to_double(uint16_t h)
+static double orc_fp16_to_double(uint16_t h)
 {
     double s = (h & 0x8000u) ? -1.0 : 1.0;
     int ex = (h >> 10) & 0x1F;
@@ -162,7 +162,7 @@ double orc_fp16_to_double(uint16_t h)
 /* OCP FP8 E4M3 ("fn"): 4 significant bits, emin = -6, max 448, no
  * infinities, S.1111.111 is NaN. Out-of-range finite values saturate to
  * +-448. */
-uint8_t orc_e4m3_from_float(float x)
+static uint8_t orc_e4m3_from_float(float x)
 {
     if (isnan(x))
         return 0x7Fu; /* one NaN code, no sign */
@@ -194,7 +194,7 @@ static float max_abs_nan(float amax, float y)
  * Finite values round to nearest, ties to even, and saturate to +-6. The
  * code is S.EE.M in the low nibble. NaN and infinities are not defined by
  * the format; here NaN maps to +-6's code like the infinities. */
-uint8_t orc_e2m1_from_float(float x)
+static uint8_t orc_e2m1_from_float(float x)
 {
     uint8_t sign = signbit(x) ? 0x8u : 0;
     if (isnan(x) || isinf(x))
@@ -212,22 +212,12 @@ uint8_t orc_e2m1_from_float(float x)
     return (uint8_t)(sign | (uint8_t)(e << 1) | mant);
 }
 
-double orc_e2m1_to_double(uint8_t c)
-{
-    double s = (c & 0x8u) ? -1.0 : 1.0;
-    int ex = (c >> 1) & 3;
-    int m = c & 1;
-    if (ex == 0)
-        return s * 0.5 * m;
-    return s * ldexp(1.0 + 0.5 * m, ex - 1);
-}
-
 /* MX shared scale of a block (OCP Microscaling Formats v1.0, section 6.3):
  * X = 2^(floor(log2(amax)) - emax_elem) with emax_elem = 2 for E2M1,
  * returned as its E8M0 code (biased exponent, bias 127), the exponent
  * clamped to [-127, 127]. An all-zero block takes 2^-127 (code 0); a block
  * with a NaN or an infinity takes the E8M0 NaN code 0xFF. */
-uint8_t orc_mx_scale_code(float amax)
+static uint8_t orc_mx_scale_code(float amax)
 {
     if (isnan(amax) || isinf(amax))
         return 0xFFu;
@@ -241,18 +231,6 @@ uint8_t orc_mx_scale_code(float amax)
     if (se > 127)
         se = 127;
     return (uint8_t)(se + 127);
-}
-
-double orc_e4m3_to_double(uint8_t q)
-{
-    double s = (q & 0x80u) ? -1.0 : 1.0;
-    int ex = (q >> 3) & 0xF;
-    int m = q & 7;
-    if (ex == 0xF && m == 7)
-        return NAN;
-    if (ex == 0)
-        return s * ldexp((double)m, -9);
-    return s * ldexp((double)(8 + m), ex - 7 - 3);
 }
 
 /* ------------------------------------------------------------------ */

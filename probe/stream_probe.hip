@@ -1,0 +1,133 @@
+// stream_probe.hip -- a data-movement-only row kernel: the measured ceiling the
+// fused epilogue's row kernel is compared with. Measurement tooling for the
+// benchmark, not part of the library.
+//
+// One block per row, tpr threads per row, each thread owning ppt 16-byte packs
+// of the row (pack lane + k * tpr). Every thread reads its packs of all nin
+// input streams (pack by pack, streams in order) with at most `window` loads in
+// flight, then writes its packs of the output streams: the last output gets the
+// last input's pack, the other outputs the XOR of the inputs (one integer
+// operation per word, so nothing is optimised away and no floating-point work is
+// done). Loads and stores are non-temporal, as in the fused kernel. Rows are
+// row_bytes long (a multiple of 16); packs past the row are skipped.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMaxIn = 9;
+constexpr int kMaxOut = 2;
+
+struct ProbeArgs {
+    const void *in[kMaxIn];
+    void *out[kMaxOut];
+    int P;  // packs per row
+    int tpr;
+};
+
+template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+template <int NIN, int NOUT, int PPT, int W>
+__global__ void __launch_bounds__(1024) probe_kernel(const ProbeArgs a)
+{
+    const long long row = blockIdx.x;
+    const int lt = threadIdx.x;
+    u32x4 x[PPT][NIN];
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const int j = lt + k * a.tpr;
+#pragma unroll
+        for (int s = 0; s < NIN; ++s) {
+            if (j < a.P)
+                x[k][s] = __builtin_nontemporal_load((const u32x4 *)a.in[s] + row * a.P + j);
+            else
+                x[k][s] = u32x4{0u, 0u, 0u, 0u};
+            wait_vm<W - 1>();
+        }
+    }
+    wait_vm<0>();
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const int j = lt + k * a.tpr;
+        if (j >= a.P)
+            continue;
+        u32x4 acc = x[k][0];
+#pragma unroll
+        for (int s = 1; s < NIN - 1; ++s)
+            acc ^= x[k][s];
+#pragma unroll
+        for (int o = NOUT - 1; o >= 0; --o)
+            __builtin_nontemporal_store(o == NOUT - 1 ? x[k][NIN - 1] : acc, (u32x4 *)a.out[o] + row * a.P + j);
+    }
+}
+
+template <int NIN, int PPT, int W> hipError_t go(const ProbeArgs &a, long long rows, hipStream_t st)
+{
+    hipLaunchKernelGGL((probe_kernel<NIN, 2, PPT, W>), dim3((unsigned)rows), dim3(a.tpr), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int NIN, int PPT> hipError_t go_w(const ProbeArgs &a, long long rows, int window, hipStream_t st)
+{
+    switch (window) {
+    case 1: return go<NIN, PPT, 1>(a, rows, st);
+    case 2: return go<NIN, PPT, 2>(a, rows, st);
+    case 3: return go<NIN, PPT, 3>(a, rows, st);
+    default: return go<NIN, PPT, 16>(a, rows, st);
+    }
+}
+
+template <int NIN> hipError_t go_p(const ProbeArgs &a, long long rows, int ppt, int window, hipStream_t st)
+{
+    switch (ppt) {
+    case 1: return go_w<NIN, 1>(a, rows, window, st);
+    case 2: return go_w<NIN, 2>(a, rows, window, st);
+    case 3: return go_w<NIN, 3>(a, rows, window, st);
+    default: return go_w<NIN, 4>(a, rows, window, st);
+    }
+}
+
+}  // namespace
+
+// Returns 0 on success, -1 for arguments it does not take (nothing launched),
+// -4 for a launch error. in: nin device pointers (2..9) to rows x row_bytes;
+// out: nout (= 2) device pointers of the same size; ppt 1..4; tpr a multiple of
+// 64, at most 1024, with tpr * ppt * 16 >= row_bytes; window 1, 2, 3 or 16.
+extern "C" __attribute__((visibility("default"))) int probe_rows(const void *const *in, int nin, void *const *out,
+                                                                 int nout, long long rows, int row_bytes, int ppt,
+                                                                 int tpr, int window, hipStream_t st)
+{
+    if (nin < 2 || nin > kMaxIn || nout != 2 || rows < 0 || rows > 0x7fffffffLL || row_bytes < 16 ||
+        row_bytes % 16 || ppt < 1 || ppt > 4 || tpr < 64 || tpr > 1024 || tpr % 64 ||
+        (long long)tpr * ppt * 16 < row_bytes || (window != 1 && window != 2 && window != 3 && window != 16))
+        return -1;
+    if (rows == 0)
+        return 0;
+    ProbeArgs a = {};
+    for (int s = 0; s < nin; ++s) {
+        if (!in[s])
+            return -1;
+        a.in[s] = in[s];
+    }
+    for (int o = 0; o < nout; ++o) {
+        if (!out[o])
+            return -1;
+        a.out[o] = out[o];
+    }
+    a.P = row_bytes / 16;
+    a.tpr = tpr;
+    hipError_t e;
+    switch (nin) {
+    case 2: e = go_p<2>(a, rows, ppt, window, st); break;
+    case 3: e = go_p<3>(a, rows, ppt, window, st); break;
+    case 4: e = go_p<4>(a, rows, ppt, window, st); break;
+    case 5: e = go_p<5>(a, rows, ppt, window, st); break;
+    case 6: e = go_p<6>(a, rows, ppt, window, st); break;
+    case 7: e = go_p<7>(a, rows, ppt, window, st); break;
+    case 8: e = go_p<8>(a, rows, ppt, window, st); break;
+    default: e = go_p<9>(a, rows, ppt, window, st); break;
+    }
+    return e == hipSuccess ? 0 : -4;
+}

@@ -1,7 +1,7 @@
 """Summaries of rocprofv3 runs of bench.py: per-kernel durations and HBM traffic.
 
 Usage (paths are the rocprofv3 output directories of one command each):
-  python -m all_reduce_residual_rank_amd.prof --trace DIR --fetch DIR --write DIR \\
+  python prof.py --trace DIR --fetch DIR --write DIR \\
       --workload NAME --path one --command "..." --out profiles/NAME.md
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same

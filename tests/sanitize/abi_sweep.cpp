@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <random>
 #include "arrms.h"
+#include "arrms_tuning.h"
 
 int main(int argc, char **argv) {
   const int n = argc > 1 ? atoi(argv[1]) : 100000;

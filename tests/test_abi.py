@@ -15,19 +15,24 @@ import pytest
 from all_reduce_residual_rank_amd import arrms
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "arrms.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 BASE = 1 << 40          # fake device addresses, far apart
 STRIDE = 1 << 32
 
 
+def _headers_text():
+    return "\n".join(open(h).read() for h in HEADERS)
+
+
 def declared_functions():
-    text = open(HEADER).read()
+    text = _headers_text()
     return sorted(set(re.findall(r"ARRMS_API\s+[\w\s\*]*?\b(arrms_\w+)\s*\(", text)))
 
 
 def header_constants():
-    text = open(HEADER).read()
+    text = _headers_text()
     out = {}
     for name, val in re.findall(r"#define\s+ARRMS_(\w+)\s+\(?(-?\d+)u?\)?\s", text):
         out[name] = int(val)
@@ -94,7 +99,7 @@ def test_invalid_arguments(kw):
     dict(H=60),                                  # 120 bytes per bf16 row: not 16-byte packs
     dict(H=6, flags=arrms.DTYPE_FP32),           # 24 bytes per fp32 row
     dict(H=arrms.MAX_HIDDEN + 8),
-    dict(H=arrms.MAX_ROW_BYTES // 4 + 4, flags=arrms.DTYPE_FP32),  # fp32 row past 32 KiB
+    dict(H=arrms.MAX_HIDDEN + 4, flags=arrms.DTYPE_FP32),  # fp32 row past the hidden cap
     dict(flags=arrms.DTYPE_FP32 | arrms.FP8),
     dict(in1=BASE + STRIDE + 8),                 # misaligned rank input
     dict(residual=BASE + 10 * STRIDE + 2),
@@ -133,10 +138,11 @@ def test_query_path():
     assert arrms.arrms_query_path(1024, 60, 4, 0) == arrms.ERR_UNSUPPORTED
     assert arrms.arrms_query_path(1024, 64, 9, 0) == arrms.ERR_INVALID
     assert arrms.arrms_query_path(16, 512, 4, arrms.DTYPE_FP32 | arrms.FP8) == arrms.ERR_UNSUPPORTED
-    # rows are capped at 32 KiB: bf16 up to the hidden cap, fp32 up to 8192
+    # every dtype up to the hidden cap (fp32: 64 KiB rows)
     assert arrms.arrms_query_path(16, 16384, 4, 0) == arrms.PATH_ONE_STAGE
-    assert arrms.arrms_query_path(16, 8192, 4, arrms.DTYPE_FP32) == arrms.PATH_ONE_STAGE
-    assert arrms.arrms_query_path(16, 8196, 4, arrms.DTYPE_FP32) == arrms.ERR_UNSUPPORTED
+    assert arrms.arrms_query_path(16, 8196, 4, arrms.DTYPE_FP32) == arrms.PATH_ONE_STAGE
+    assert arrms.arrms_query_path(16, 16384, 8, arrms.DTYPE_FP32) == arrms.PATH_ONE_STAGE
+    assert arrms.arrms_query_path(16, 16388, 4, arrms.DTYPE_FP32) == arrms.ERR_UNSUPPORTED
 
 
 def _call_strided(R=4, M=8, H=64, flags=0, eps=1e-6, ld=(64, 64, 64, 64, 64), **over):

@@ -37,3 +37,16 @@ def test_abi_host_code_is_sanitizer_clean(tmp_path):
     assert r.returncode == 0, report[-3000:]
     assert "runtime error" not in report and "AddressSanitizer" not in report, report[-3000:]
     assert "calls 60000" in report
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_staging_bookkeeping(tmp_path):
+    """Growing the staging buffer retires the old one (kept allocated for graphs
+    captured earlier); release frees each buffer exactly once."""
+    exe = str(tmp_path / "staging_test")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=undefined", f"-I{CSRC}", os.path.join(HERE, "staging_test.cpp"),
+                    "-o", exe], check=True, capture_output=True, text=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "staging ok" in r.stdout

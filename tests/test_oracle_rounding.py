@@ -120,3 +120,28 @@ def test_quant_rows_scale_is_fp32_division(dt):
     for m in range(5):
         j = np.argmax(np.abs(vals[m]))
         assert q[m, j] & 0x7F == 0x7E
+
+
+# Each exported function of liboracle.so, with a test in this suite that pins it
+# against something other than the oracle itself (format tables, library casts,
+# closed forms, brute force).
+PINNED_EXPORTS = {
+    "oracle_fused_rows": "test_oracle_fused.py (closed forms, exact-rational brute force, torch fp64 RMSNorm)",
+    "oracle_rank_sum": "test_oracle_rank_sum.py (rank-order witness, exact integers, torch fp32 sums)",
+    "oracle_quant_rows": "test_oracle_fused.py / test_oracle_group_quant.py (E4M3 table, amax/448)",
+    "orc_bf16_from_double_n": "test_bf16_matches_torch_cast_on_float32 and the table search",
+    "orc_fp16_from_double_n": "the numpy float64 -> float16 cast and the table search",
+    "orc_e4m3_from_float_n": "the torch float8_e4m3fn cast and the table search",
+    "orc_e2m1_from_float_n": "test_oracle_group_quant.py (E2M1 table search)",
+}
+
+
+def test_every_oracle_export_is_pinned():
+    """The oracle library exports exactly the functions listed above: a new or
+    leftover export without a pin fails here."""
+    import subprocess
+    oracle._load()
+    out = subprocess.run(["nm", "-D", "--defined-only", oracle._LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if len(ln.split()) == 3 and ln.split()[1] == "T"}
+    assert exported == set(PINNED_EXPORTS)

@@ -153,11 +153,20 @@ def test_hidden_sizes_and_tails(H):
     _case(wl, 5, ("one", "two"))
 
 
-@pytest.mark.parametrize("H", [8188, 8192])
+@pytest.mark.parametrize("H", [8188, 8192, 12284, 16380, 16384])
 def test_widest_fp32_rows(H):
-    # fp32 rows up to the 32 KiB row cap (2048 packs), ragged and exact
+    # fp32 rows up to the hidden cap (64 KiB, 4096 packs: blocks of 1024 threads),
+    # ragged and exact
     wl = wlmod.Workload("fp32wide", R=4, M=11, H=H, dtype="fp32", gemma=True, w_mean=0.0)
     _case(wl, 9, ("one", "two"))
+
+
+@pytest.mark.parametrize("R,M", [(8, 7), (1, 600), (3, 300)])
+def test_fp32_hidden_cap_rank_counts(R, M):
+    # the widest fp32 rows at the extreme rank counts (R = 8 takes more packs per
+    # thread than the register budget asks for), and launches of several hundred rows
+    wl = wlmod.Workload("fp32cap", R=R, M=M, H=16384, dtype="fp32")
+    _case(wl, 11 + R, ("one", "two"))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
