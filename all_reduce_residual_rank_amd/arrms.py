@@ -49,7 +49,7 @@ FP8_GROUP_SIZE = 128
 MX_BLOCK = 32
 
 EXPORTS = ("arrms_fused", "arrms_fused_strided", "arrms_fused_quant", "arrms_allreduce_sum",
-           "arrms_fused_config",
+           "arrms_fused_config", "arrms_query_launch", "arrms_plan_launch",
            "arrms_reserve_staging", "arrms_release_staging", "arrms_staging_bytes", "arrms_query_path",
            "arrms_status_string")
 
@@ -68,6 +68,10 @@ _lib.arrms_allreduce_sum.restype = _i
 _lib.arrms_fused_config.argtypes = [ctypes.POINTER(_vp), _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i,
                                     _i, _i, _i, _i, _i, _vp]
 _lib.arrms_fused_config.restype = _i
+_lib.arrms_query_launch.argtypes = [_i, _i, _i, _i, _i, _i, ctypes.POINTER(_i)]
+_lib.arrms_query_launch.restype = _i
+_lib.arrms_plan_launch.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, ctypes.POINTER(_i)]
+_lib.arrms_plan_launch.restype = _i
 _lib.arrms_reserve_staging.argtypes = [_sz]
 _lib.arrms_reserve_staging.restype = _i
 _lib.arrms_release_staging.argtypes = []
@@ -310,6 +314,31 @@ def arrms_allreduce_sum(rank_in, out, *, flags: int, n: int | None = None, strea
     rc = arrms_allreduce_sum_raw(rank_in, len(rank_in), out, n, flags, _stream_handle(stream))
     if rc != OK:
         raise ArrmsError(rc, "arrms_allreduce_sum")
+
+
+LAUNCH_INFO = 8
+LAUNCH_FIELDS = ("path", "ppt", "tpr", "rpb", "window", "cap16", "blocks_per_cu", "cus")
+
+
+def arrms_query_launch(M: int, H: int, R: int, flags: int, quant: int = 0, mirror: bool = False) -> dict:
+    """The row-kernel launch arrms_fused makes for these sizes on the current
+    device (arrms_tuning.h), as a dict of LAUNCH_FIELDS."""
+    info = (_i * LAUNCH_INFO)()
+    rc = _lib.arrms_query_launch(int(M), int(H), int(R), int(flags), int(quant), int(bool(mirror)), info)
+    if rc != OK:
+        raise ArrmsError(rc, "arrms_query_launch")
+    return dict(zip(LAUNCH_FIELDS, list(info)))
+
+
+def arrms_plan_launch(M: int, H: int, R: int, flags: int, quant: int, mirror: bool, blocks_per_cu: int,
+                      cus: int) -> dict:
+    """The same launch from given device facts (pure host)."""
+    info = (_i * LAUNCH_INFO)()
+    rc = _lib.arrms_plan_launch(int(M), int(H), int(R), int(flags), int(quant), int(bool(mirror)),
+                                int(blocks_per_cu), int(cus), info)
+    if rc != OK:
+        raise ArrmsError(rc, "arrms_plan_launch")
+    return dict(zip(LAUNCH_FIELDS, list(info)))
 
 
 def arrms_reserve_staging(nbytes: int = 0) -> None:

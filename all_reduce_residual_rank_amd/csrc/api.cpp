@@ -11,6 +11,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "arrms.h"
@@ -26,7 +27,7 @@ using arrms::DT_FP32;
 
 constexpr int kKnownFlags = ARRMS_DTYPE_MASK | ARRMS_GEMMA | ARRMS_FP8 | ARRMS_FORCE_ONE_STAGE |
                             ARRMS_FORCE_TWO_STAGE | ARRMS_EXACT_ONLY;
-constexpr int kMaxDevices = 64;
+using arrms::kMaxDevices;
 
 int esize(int dt) { return dt == DT_FP32 ? 4 : 2; }
 
@@ -219,7 +220,7 @@ arrms::RowShape choose_shape(int P, int R, long long M, bool fp8, bool fp32)
     // fp32 kernels take blocks of up to 1024 threads at any PPT (rows of up to
     // 4096 packs); the others at one pack per thread only
     const int wide_block = fp32 ? 1024 : 512;
-    arrms::RowShape best = {0, 0, 0, false, 0, 0};
+    arrms::RowShape best = {0, 0, 0, false, 0, 0, false};
     long long best_key = -1;
     int cap = fp8 ? 3 : 4;
     if (M < 512 && cap > 2)
@@ -245,7 +246,7 @@ arrms::RowShape choose_shape(int P, int R, long long M, bool fp8, bool fp32)
         const long long key = (long long)waste * 16 + (4 - ppt);
         if (best_key < 0 || key < best_key) {
             best_key = key;
-            best = {ppt, tpr, 1, waste != 0, 0, 0};
+            best = {ppt, tpr, 1, waste != 0, 0, 0, false};
         }
     }
     if (best.ppt == 0) {
@@ -254,7 +255,7 @@ arrms::RowShape choose_shape(int P, int R, long long M, bool fp8, bool fp32)
             int tpr = (P + ppts[c] - 1) / ppts[c];
             tpr = (tpr + 63) / 64 * 64;
             if (tpr <= wide_block)
-                best = {ppts[c], tpr, 1, tpr * ppts[c] != P, 0, 0};
+                best = {ppts[c], tpr, 1, tpr * ppts[c] != P, 0, 0, false};
         }
     }
     if (best.ppt == 0)
@@ -286,6 +287,88 @@ hipError_t launch_row(int dt, int quant, bool mirror, const arrms::RowArgs &a, i
     default:
         return arrms::launch_row_fp32_t(a, R, s, st);
     }
+}
+
+int row_occupancy(int dt, int quant, bool mirror, int R, const arrms::RowShape &s)
+{
+    switch (dt) {
+    case DT_BF16:
+        switch (quant) {
+        case Q_NONE: return arrms::occupancy_row_bf16_t(R, s);
+        case Q_TOKEN: return mirror ? arrms::occupancy_row_bf16_fp8t(R, s) : arrms::occupancy_row_bf16_fp8(R, s);
+        case Q_GROUP: return arrms::occupancy_row_bf16_fp8g(R, s);
+        default: return arrms::occupancy_row_bf16_mx4(R, s);
+        }
+    case DT_FP16:
+        switch (quant) {
+        case Q_NONE: return arrms::occupancy_row_fp16_t(R, s);
+        case Q_TOKEN: return mirror ? arrms::occupancy_row_fp16_fp8t(R, s) : arrms::occupancy_row_fp16_fp8(R, s);
+        case Q_GROUP: return arrms::occupancy_row_fp16_fp8g(R, s);
+        default: return arrms::occupancy_row_fp16_mx4(R, s);
+        }
+    default:
+        return arrms::occupancy_row_fp32_t(R, s);
+    }
+}
+
+// Compute units of the current device (cached per device; 0 if the runtime
+// cannot tell).
+int device_cus()
+{
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return 0;
+        }
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// A launch is "large" when its input streams exceed 16 MiB: then the load
+// window, not the size of the launch, sets how many bytes are in flight.
+bool large_launch(int R, long long rows, int P) { return (long long)(R + 1) * rows * P * 16 > (16ll << 20); }
+
+// Load window and occupancy cap of a row-kernel launch over `rows` rows of P
+// packs with R input ranks, shape s; resident = blocks of this shape (narrow
+// window) the device holds at once. An explicit window (s.window != 0) is kept.
+//  * The narrow window when the whole launch is resident at once, it is large
+//    and a row has at most 6 input streams; the wide window otherwise
+//    (resident 1024 x 6144 bf16 rows: R = 5 17.8 us narrow, 19.0 wide; R = 6
+//    21.4 narrow, 21.0 wide; R = 8 25.1 narrow, 24.7 wide).
+//  * The occupancy cap (at most 16 waves per compute unit) for large
+//    wide-window launches of 6 or more input streams per row that run in
+//    several rounds of blocks: R = 5, 6, 7, 8 at 2048 x 7168 bf16 41.1 -> 39.6,
+//    46.1 -> 44.3, 50.8 -> 48.9, 55.9 -> 54.3 us; R = 8 at 2048 x 6144 47.6 ->
+//    46.6; R = 8 at 4096 x 4096 equal. With 5 streams it measured mixed (2800 x
+//    6144 fp16 rows -0.1 us, 2048 x 7168 bf16 +0.25 us, the FP8 epilogue +0.2
+//    us), so R <= 4 keeps the full occupancy.
+void plan_window(arrms::RowShape &s, int R, long long rows, int P, long long resident)
+{
+    const long long groups = (rows + s.rpb - 1) / s.rpb;
+    const long long grid = (s.grid > 0 && s.grid < groups) ? s.grid : groups;
+    const bool large = large_launch(R, rows, P);
+    if (s.window == 0)
+        s.window = large && grid <= resident && R <= 5 ? 1 : 2;
+    s.cap16 = s.window == 2 && large && grid > resident && R >= 5;
+}
+
+// Resident blocks of shape s on the current device (narrow-window kernel), or
+// 0 when the launch is not large (the rules then do not need it).
+long long resident_blocks(int dt, int quant, bool mirror, int R, long long rows, int P, const arrms::RowShape &s)
+{
+    if (!large_launch(R, rows, P))
+        return 0;
+    arrms::RowShape q = s;
+    q.window = 1;
+    return (long long)row_occupancy(dt, quant, mirror, R, q) * device_cus();
 }
 
 hipError_t launch_flat(int dt, const arrms::FlatArgs &a, int R, hipStream_t st)
@@ -492,19 +575,20 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
         arrms::RowShape s = choose_shape(P, R, M, fp8, dt == DT_FP32);
         if (s.ppt == 0 || !apply_shape(req, P, R, M, dt == DT_FP32, s))
             return ARRMS_ERR_UNSUPPORTED;
+        plan_window(s, R, M, P, resident_blocks(dt, quant, out != nullptr, R, M, P, s));
         a.tpr = s.tpr;
         return launch_row(dt, quant, out != nullptr, a, R, s, stream) == hipSuccess ? ARRMS_OK : ARRMS_ERR_HIP;
     }
 
     // ---- two-stage: per row chunk, flat rank reduce into staging, then the
     // row pass with the staging rows as its single input.
-    int dev;
-    rc = current_device(&dev);
-    if (rc != ARRMS_OK)
-        return rc;
     void *staging;
     size_t staging_bytes;
     {
+        int dev;
+        rc = current_device(&dev);
+        if (rc != ARRMS_OK)
+            return rc;
         std::lock_guard<std::mutex> lk(g_staging_mu);
         if (!g_staging.ptr(dev)) {
             hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -568,6 +652,7 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
         arrms::RowShape s = choose_shape(P, R, M, fp8, dt == DT_FP32);
         if (s.ppt == 0 || !apply_shape(req, P, R, n, dt == DT_FP32, s))
             return ARRMS_ERR_UNSUPPORTED;
+        plan_window(s, 1, n, P, resident_blocks(dt, quant, out != nullptr, 1, n, P, s));
         b.tpr = s.tpr;
         if (launch_row(dt, quant, out != nullptr, b, 1, s, stream) != hipSuccess)
             return ARRMS_ERR_HIP;
@@ -610,6 +695,86 @@ int arrms_fused_config(const void *const *rank_in, int R, const void *residual, 
     const Strides ld = {H, H, H, H, H};
     return fused_impl(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H, eps,
                       flags, ld, &req, stream, (flags & ARRMS_FP8) ? Q_TOKEN : Q_NONE);
+}
+
+}  // extern "C"
+
+namespace {
+
+// arrms_query_launch / arrms_plan_launch: bpc < 0 asks the current device.
+int plan_launch(int M, int H, int R, int flags, int quant, int mirror, int bpc, int cus, int *info)
+{
+    if (!info)
+        return ARRMS_ERR_INVALID;
+    if (flags & ARRMS_FP8) {
+        if (quant != 0 && quant != ARRMS_QUANT_FP8_TOKEN)
+            return ARRMS_ERR_INVALID;
+        quant = ARRMS_QUANT_FP8_TOKEN;
+        flags &= ~ARRMS_FP8;
+    }
+    if (quant < 0 || quant > ARRMS_QUANT_MXFP4)
+        return ARRMS_ERR_INVALID;
+    const int q = quant == 0 ? Q_NONE : quant == ARRMS_QUANT_FP8_TOKEN ? Q_TOKEN : quant == ARRMS_QUANT_FP8_GROUP ? Q_GROUP : Q_MX;
+    int rc = validate_sizes(M, H, R, flags | (q != Q_NONE ? ARRMS_FP8 : 0));
+    if (rc != ARRMS_OK)
+        return rc;
+    if ((q == Q_GROUP && H % ARRMS_FP8_GROUP_SIZE) || (q == Q_MX && H % ARRMS_MX_BLOCK))
+        return ARRMS_ERR_UNSUPPORTED;
+    for (int i = 0; i < ARRMS_LAUNCH_INFO; ++i)
+        info[i] = 0;
+    const int path = choose_path(M, H, R, flags);
+    info[0] = path;
+    if (path == ARRMS_PATH_NONE)
+        return ARRMS_OK;
+    const int dt = flags & ARRMS_DTYPE_MASK;
+    const int e = esize(dt);
+    const int P = H * e / 16;
+    long long rows = M;
+    int Rr = R;
+    if (path == ARRMS_PATH_TWO_STAGE) {
+        const long long cap = (long long)(ARRMS_DEFAULT_STAGING_BYTES / ((size_t)H * (size_t)e));
+        const long long nchunks = (M + cap - 1) / cap;
+        rows = (M + nchunks - 1) / nchunks;
+        Rr = 1;
+    }
+    arrms::RowShape s = choose_shape(P, R, M, q != Q_NONE, dt == DT_FP32);
+    if (s.ppt == 0)
+        return ARRMS_ERR_UNSUPPORTED;
+    long long resident;
+    if (bpc < 0) {
+        arrms::RowShape n = s;
+        n.window = 1;
+        bpc = row_occupancy(dt, q, mirror != 0, Rr, n);
+        cus = device_cus();
+        resident = resident_blocks(dt, q, mirror != 0, Rr, rows, P, s);
+    } else {
+        resident = large_launch(Rr, rows, P) ? (long long)bpc * cus : 0;
+    }
+    plan_window(s, Rr, rows, P, resident);
+    info[1] = s.ppt;
+    info[2] = s.tpr;
+    info[3] = s.rpb;
+    info[4] = s.window;
+    info[5] = s.cap16 ? 1 : 0;
+    info[6] = bpc;
+    info[7] = cus;
+    return ARRMS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int arrms_query_launch(int M, int H, int R, int flags, int quant, int mirror, int *info)
+{
+    return plan_launch(M, H, R, flags, quant, mirror, -1, 0, info);
+}
+
+int arrms_plan_launch(int M, int H, int R, int flags, int quant, int mirror, int blocks_per_cu, int cus, int *info)
+{
+    if (blocks_per_cu < 0 || cus < 0)
+        return ARRMS_ERR_INVALID;
+    return plan_launch(M, H, R, flags, quant, mirror, blocks_per_cu, cus, info);
 }
 
 int arrms_fused_quant(const void *const *rank_in, int R, const void *residual, const void *weight,

@@ -8,4 +8,9 @@ hipError_t launch_row_bf16_fp8t(const RowArgs &a, int R, const RowShape &s, hipS
     return row_launch_epi<DT_BF16, EPI_FP8_T>(a, R, s, st);
 }
 
+int occupancy_row_bf16_fp8t(int R, const RowShape &s)
+{
+    return row_occupancy_epi<DT_BF16, EPI_FP8_T>(R, s);
+}
+
 }  // namespace arrms

@@ -8,4 +8,9 @@ hipError_t launch_row_fp16_fp8g(const RowArgs &a, int R, const RowShape &s, hipS
     return row_launch_epi<DT_FP16, EPI_FP8G>(a, R, s, st);
 }
 
+int occupancy_row_fp16_fp8g(int R, const RowShape &s)
+{
+    return row_occupancy_epi<DT_FP16, EPI_FP8G>(R, s);
+}
+
 }  // namespace arrms

@@ -8,6 +8,11 @@ hipError_t launch_row_fp16_t(const RowArgs &a, int R, const RowShape &s, hipStre
     return row_launch_epi<DT_FP16, EPI_T>(a, R, s, st);
 }
 
+int occupancy_row_fp16_t(int R, const RowShape &s)
+{
+    return row_occupancy_epi<DT_FP16, EPI_T>(R, s);
+}
+
 hipError_t launch_flat_fp16(const FlatArgs &a, int R, hipStream_t st)
 {
     return flat_launch<DT_FP16>(a, R, st);

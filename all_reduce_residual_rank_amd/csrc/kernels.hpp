@@ -929,31 +929,17 @@ __global__ void __launch_bounds__(kFlatThreads) flat_kernel(const FlatArgs a)
 // --------------------------------------------------------------------------
 // Launch helpers (instantiated per dtype by kern_*.hip).
 
-// Compute units of the current device (cached per device).
-static int device_cus()
-{
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 0;
-    int n = cache[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return 0;
-        cache[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 // LDS bytes of one compute unit and the most one block may reserve (cached
 // per device; 0 if the runtime cannot tell).
 static void device_lds(int &per_cu, int &per_block)
 {
-    static std::atomic<int> cu_cache[64], blk_cache[64];
+    static std::atomic<int> cu_cache[kMaxDevices], blk_cache[kMaxDevices];
     per_cu = per_block = 0;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
         return;
+    }
     int c = cu_cache[dev].load(std::memory_order_relaxed), b = blk_cache[dev].load(std::memory_order_relaxed);
     if (c == 0 || b == 0) {
         if (hipDeviceGetAttribute(&c, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
@@ -968,82 +954,107 @@ static void device_lds(int &per_cu, int &per_block)
     per_block = b;
 }
 
-// Blocks of row_kernel<.., window_low<R>()> one compute unit holds at this block
-// size (cached per block size; 0 if the runtime cannot tell).
+// Blocks of row_kernel<DT, R, PPT, EPI, window> one compute unit of the current
+// device holds at this block size (0 if the runtime cannot tell). Cached per
+// device, window (1 narrow, 2 wide, 3 medium) and block size.
 template <int DT, int R, int PPT, int EPI>
-static int blocks_per_cu(int block)
+static int row_occupancy(int block, int win)
 {
-    static std::atomic<int> cache[1024 / 64 + 1];
-    const int slot = block / 64;
-    int n = cache[slot].load(std::memory_order_relaxed);
+    static std::atomic<uint8_t> cache[kMaxDevices][3][1024 / 64 + 1];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    if (block < 64 || block > 1024 || block % 64 != 0 || win < 1 || win > 3)
+        return 0;
+    std::atomic<uint8_t> &slot = cache[dev][win - 1][block / 64];
+    int n = slot.load(std::memory_order_relaxed);
     if (n == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_kernel<DT, R, PPT, EPI, window_low<R>()>, block, 0) !=
-            hipSuccess) {
+        hipError_t e;
+        if (win == 1)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_kernel<DT, R, PPT, EPI, window_low<R>()>, block, 0);
+        else if (win == 3 && (R + 1) * PPT > kWindowMid)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_kernel<DT, R, PPT, EPI, kWindowMid>, block, 0);
+        else
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, row_kernel<DT, R, PPT, EPI, kWindowHigh>, block, 0);
+        if (e != hipSuccess || n <= 0 || n > 255) {
             (void)hipGetLastError();
             return 0;
         }
-        cache[slot].store(n, std::memory_order_relaxed);
+        slot.store((uint8_t)n, std::memory_order_relaxed);
     }
     return n;
 }
 
+// Launch of a planned shape (api.cpp sets every field: the window, and cap16 for
+// launches that hold at most 16 waves per compute unit).
 template <int DT, int R, int PPT, int EPI>
 static hipError_t row_go(const RowArgs &a, const RowShape &s, hipStream_t st)
 {
     const int block = s.tpr * s.rpb;
     const long long groups = (a.M + s.rpb - 1) / s.rpb;
     const long long grid = (s.grid > 0 && s.grid < groups) ? s.grid : groups;
-    if (grid > 0x7fffffffLL || block > row_max_block<DT, PPT>() || s.tpr != a.tpr)
+    if (grid > 0x7fffffffLL || block > row_max_block<DT, PPT>() || s.tpr != a.tpr || s.window < 1 || s.window > 3)
         return hipErrorInvalidValue;
     RowArgs b = a;
     b.rpb = s.rpb;
     b.groups = groups;
-    const long long input = (long long)(R + 1) * a.M * a.P * 16;
-    const bool large = input > (16ll << 20);
-    const long long resident = large ? (long long)blocks_per_cu<DT, R, PPT, EPI>(block) * device_cus() : 0;
-    int win = s.window;  // 1 narrow, 2 wide, 3 medium
-    if (win == 0) {
-        // the narrow window when the whole launch is resident at once, its
-        // input streams exceed 16 MiB (then the window, not the launch size,
-        // sets the bytes in flight) and a row has at most 6 of them; the wide
-        // window for the others (resident 1024 x 6144 bf16 rows: R = 5 17.8
-        // us narrow, 19.0 wide; R = 6 21.4 narrow, 21.0 wide; R = 8 25.1
-        // narrow, 24.7 wide)
-        win = large && grid <= resident && R <= 5 ? 1 : 2;
-    }
-    // A large launch of 6 or more input streams per row that runs in several
-    // rounds of blocks with the wide window: at most 16 waves per compute
-    // unit, by reserving enough LDS per block that no more blocks fit (the
-    // kernel itself uses none of it). Measured: R = 5, 6, 7, 8 at 2048 x
-    // 7168 bf16 41.1 -> 39.6, 46.1 -> 44.3, 50.8 -> 48.9, 55.9 -> 54.3 us;
-    // R = 8 at 2048 x 6144 47.6 -> 46.6; R = 8 at 4096 x 4096 equal. With 5
-    // streams it measured mixed (2800 x 6144 fp16 rows -0.1 us, 2048 x 7168
-    // bf16 +0.25 us, the FP8 epilogue +0.2 us at 16 waves and +2.4 at 12), so
-    // R <= 4 keeps the full occupancy.
+    // The occupancy cap: LDS that the kernel does not use, reserved so that no
+    // more blocks fit than 16 waves per compute unit. Only for blocks of at most
+    // 512 threads: the reservation then stays below 64 KiB, which a launch may
+    // take without a per-kernel attribute.
     size_t smem = 0;
-    if (win == 2 && large && grid > resident && R >= 5) {
+    if (s.cap16) {
         int lds_cu = 0, lds_block = 0;
         device_lds(lds_cu, lds_block);
         const int cap = 1024 / block;  // blocks per compute unit for 16 waves
         const size_t want = (size_t)lds_cu / (size_t)(cap + 1) + 1;  // cap + 1 blocks do not fit
-        // blocks of at most 512 threads (cap >= 2): the reservation stays below
-        // 64 KiB, which a launch may take without a per-kernel attribute
         if (cap >= 2 && lds_cu > 0 && want <= (size_t)lds_block && want <= (64u << 10))
             smem = (want + 255) & ~(size_t)255;
     }
     const dim3 g((unsigned)grid), t((unsigned)block);
-    if (win == 1) {
-        hipLaunchKernelGGL((row_kernel<DT, R, PPT, EPI, window_low<R>()>), g, t, 0, st, b);
-    } else if (win == 3) {
+    if (s.window == 1) {
+        hipLaunchKernelGGL((row_kernel<DT, R, PPT, EPI, window_low<R>()>), g, t, smem, st, b);
+    } else if (s.window == 3) {
         // rows of at most kWindowMid loads per thread: the medium window is the wide one
         if constexpr ((R + 1) * PPT > kWindowMid)
-            hipLaunchKernelGGL((row_kernel<DT, R, PPT, EPI, kWindowMid>), g, t, 0, st, b);
+            hipLaunchKernelGGL((row_kernel<DT, R, PPT, EPI, kWindowMid>), g, t, smem, st, b);
         else
-            hipLaunchKernelGGL((row_kernel<DT, R, PPT, EPI, kWindowHigh>), g, t, 0, st, b);
+            hipLaunchKernelGGL((row_kernel<DT, R, PPT, EPI, kWindowHigh>), g, t, smem, st, b);
     } else {
         hipLaunchKernelGGL((row_kernel<DT, R, PPT, EPI, kWindowHigh>), g, t, smem, st, b);
     }
     return hipGetLastError();
+}
+
+template <int DT, int R, int EPI>
+static int row_occupancy_r(const RowShape &s)
+{
+    const int block = s.tpr * s.rpb;
+    switch (s.ppt) {
+    case 1: return row_occupancy<DT, R, 1, EPI>(block, s.window);
+    case 2: return row_occupancy<DT, R, 2, EPI>(block, s.window);
+    case 3: return row_occupancy<DT, R, 3, EPI>(block, s.window);
+    case 4: return row_occupancy<DT, R, 4, EPI>(block, s.window);
+    default: return 0;
+    }
+}
+
+template <int DT, int EPI>
+static int row_occupancy_epi(int R, const RowShape &s)
+{
+    switch (R) {
+    case 1: return row_occupancy_r<DT, 1, EPI>(s);
+    case 2: return row_occupancy_r<DT, 2, EPI>(s);
+    case 3: return row_occupancy_r<DT, 3, EPI>(s);
+    case 4: return row_occupancy_r<DT, 4, EPI>(s);
+    case 5: return row_occupancy_r<DT, 5, EPI>(s);
+    case 6: return row_occupancy_r<DT, 6, EPI>(s);
+    case 7: return row_occupancy_r<DT, 7, EPI>(s);
+    case 8: return row_occupancy_r<DT, 8, EPI>(s);
+    default: return 0;
+    }
 }
 
 template <int DT, int R, int EPI>

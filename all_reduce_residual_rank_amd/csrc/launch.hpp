@@ -11,6 +11,7 @@ namespace arrms {
 enum Dtype { DT_BF16 = 0, DT_FP16 = 1, DT_FP32 = 2 };
 
 constexpr int kMaxRanks = 8;
+constexpr int kMaxDevices = 64;
 constexpr int kMaxWavesPerBlock = 16;  // row kernel blocks are at most 1024 threads
 
 // Arguments of the row kernel (one-stage, and stage 2 of two-stage with R = 1
@@ -57,7 +58,9 @@ struct FlatArgs {
 // rpb rows side by side per block; tail = tpr * PPT > packs per row. grid is
 // the number of blocks: 0 (or at least the number of row groups) gives one
 // block per group of rpb rows; fewer blocks each take every grid-th group in
-// turn. window: phase-1 load window, 0 automatic, 1 narrow, 2 wide, 3 medium.
+// turn. window: phase-1 load window, 1 narrow, 2 wide, 3 medium (0 while the
+// plan is open: the launch needs one of 1..3). cap16: hold at most 16 waves
+// per compute unit (an LDS reservation the kernel does not use).
 struct RowShape {
     int ppt;
     int tpr;
@@ -65,6 +68,7 @@ struct RowShape {
     bool tail;
     int grid;
     int window;
+    bool cap16;
 };
 
 constexpr int kFlatThreads = 256;
@@ -87,6 +91,20 @@ hipError_t launch_row_bf16_fp8g(const RowArgs &a, int R, const RowShape &s, hipS
 hipError_t launch_row_bf16_mx4(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
 hipError_t launch_row_fp16_fp8g(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
 hipError_t launch_row_fp16_mx4(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
+// Blocks of the row kernel of that shape (its tpr * rpb threads and its load
+// window) that one compute unit of the current device holds; 0 if the runtime
+// cannot tell. Cached per device.
+int occupancy_row_bf16_fp8(int R, const RowShape &s);
+int occupancy_row_bf16_fp8g(int R, const RowShape &s);
+int occupancy_row_bf16_fp8t(int R, const RowShape &s);
+int occupancy_row_bf16_mx4(int R, const RowShape &s);
+int occupancy_row_bf16_t(int R, const RowShape &s);
+int occupancy_row_fp16_fp8(int R, const RowShape &s);
+int occupancy_row_fp16_fp8g(int R, const RowShape &s);
+int occupancy_row_fp16_fp8t(int R, const RowShape &s);
+int occupancy_row_fp16_mx4(int R, const RowShape &s);
+int occupancy_row_fp16_t(int R, const RowShape &s);
+int occupancy_row_fp32_t(int R, const RowShape &s);
 hipError_t launch_flat_bf16(const FlatArgs &a, int R, hipStream_t st);
 hipError_t launch_flat_fp16(const FlatArgs &a, int R, hipStream_t st);
 hipError_t launch_flat_fp32(const FlatArgs &a, int R, hipStream_t st);

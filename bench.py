@@ -13,11 +13,19 @@ Timing protocol (every figure below):
               of a fresh process keeps falling over its first few hundred calls
               while clocks and memory settle (reported as preroll_calls);
   warm-up     then --warmup further calls, untimed;
-  timed       exactly --steps calls: one replay of the graph between two HIP
-              events. The replay is queued behind a short GPU spin and one
-              untimed lead-in replay, so the host's graph-launch latency never
-              falls between the events: the figure is the GPU time of back-to-
-              back calls. Further replays, queued the same way, give the spread.
+  timed       exactly --steps calls of the entry point, eager, on one stream,
+              between two HIP events. Each block of timed calls is queued behind
+              untimed filler on the same stream (replays of a graph of the same
+              calls), long enough that the host has issued the whole block
+              before the GPU reaches its first event: the figure is the GPU time
+              of back-to-back calls, with no host launch gap and no per-graph
+              launch cost inside. Further blocks, queued the same way, give the
+              spread (replays). This is the headline's own measurement; every
+              other figure (other workloads and paths, the quant forms, the sum,
+              the probe, the sweep) is the us per call inside graphs of at least
+              64 calls replayed back to back (time_graph_calls), because the
+              host's cost per eager call (tens of us) would outrun the GPU's for
+              small launches; graph_us_per_call gives the headline that way too.
 
 Prints one JSON line:
   value       achieved GB/s by the metric's byte count (R+2)*M*H*2 + H*2
@@ -59,7 +67,7 @@ PEAK_GBS = 8000.0
 ROTATE_BYTES = 512 << 20
 PREROLL_CALLS = 4096
 PREROLL_SECONDS = 0.5
-MAX_GRAPH_CALLS = 4096       # small workloads: more calls per graph, so that more distinct data is touched
+MAX_TIMED_CALLS = 4096       # small workloads: more timed calls, so that more distinct data is touched
 BANDWIDTH_BOUND_BYTES = 32 << 20   # per call: below this a launch is latency-bound (report us only)
 
 
@@ -92,6 +100,14 @@ def parse():
                    help="time only the plain rank all-reduce (R=4, 1024 x 6144 bf16 message)")
     p.add_argument("--probe-only", action="store_true",
                    help="time only the data-movement probe of the chosen workload")
+    p.add_argument("--sweep", action="store_true",
+                   help="time every launch shape, load window and path of the row kernel over a grid of "
+                        "rows x hidden x ranks (bf16 T output, fp16 gemma per-token FP8) and write a CSV")
+    p.add_argument("--sweep-out", default=os.path.join(ROOT, "profiles", "dispatch_sweep.csv"))
+    p.add_argument("--sweep-m", default="1,16,64,256,1024,2800,4096")
+    p.add_argument("--sweep-h", default="512,2880,4096,6144,7168,8192")
+    p.add_argument("--sweep-r", default="2,4,8")
+    p.add_argument("--sweep-kinds", default="bf16,fp16_fp8")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 256 MiB device-to-device copy (4 times) so that a "
                         "profiler's FETCH_SIZE/WRITE_SIZE can be scaled by a kernel of known size")
@@ -141,41 +157,21 @@ def load_traffic(workload: str, path: str, digest: str):
 
 # ---- timing ----------------------------------------------------------------
 
-_SPIN_CYCLES_PER_US = None
-
-
-def _spin_rate(torch):
-    """Cycles of torch.cuda._sleep per microsecond on this GPU (measured once)."""
-    global _SPIN_CYCLES_PER_US
-    if _SPIN_CYCLES_PER_US is None:
-        cyc = 1 << 20
-        torch.cuda._sleep(cyc)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        torch.cuda._sleep(cyc)
-        e1.record()
-        torch.cuda.synchronize()
-        _SPIN_CYCLES_PER_US = cyc / max(e0.elapsed_time(e1) * 1000.0, 1.0)
-    return _SPIN_CYCLES_PER_US
-
-
 class Graph:
     """`ncalls` calls (cycling through `calls`) captured in one HIP graph on a
-    side stream."""
+    side stream: the pre-roll, and the untimed filler that keeps the GPU busy
+    while the host queues the timed calls."""
 
-    def __init__(self, torch, calls, ncalls):
+    def __init__(self, torch, calls, ncalls, stream):
         self.torch = torch
         self.ncalls = ncalls
-        self.s = torch.cuda.Stream()
-        self.s.wait_stream(torch.cuda.current_stream())
+        self.s = stream
         self.g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.g, stream=self.s):
             for i in range(ncalls):
                 calls[i % len(calls)](self.s)
         torch.cuda.synchronize()
-        self.host_launch_s = None
+        self.gpu_s = None  # GPU time of one replay
 
     def replay(self, n=1):
         with self.torch.cuda.stream(self.s):
@@ -184,73 +180,100 @@ class Graph:
 
     def preroll(self, min_calls=PREROLL_CALLS, min_seconds=PREROLL_SECONDS):
         """Untimed replays until at least min_calls calls and min_seconds have run;
-        returns the number of calls. Also measures the host's launch time of one
-        replay (for the spin that keeps it out of the timed region)."""
+        returns the number of calls. Also times one replay on the GPU."""
         torch = self.torch
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         done = 0
-        launch = []
-        batch = max(1, 64 // self.ncalls)
+        batch = max(1, 256 // self.ncalls)
         while done < min_calls or time.perf_counter() - t0 < min_seconds:
-            for _ in range(batch):
-                h0 = time.perf_counter()
-                self.replay()
-                launch.append(time.perf_counter() - h0)
-                done += self.ncalls
+            self.replay(batch)
+            done += batch * self.ncalls
             torch.cuda.synchronize()
-        self.host_launch_s = statistics.median(launch)
-        return done
-
-    def timed(self, nrep):
-        """Times nrep back-to-back replays between HIP events: a GPU spin long
-        enough for the host to queue everything, one untimed lead-in replay,
-        then the timed replays. Returns the ms of each."""
-        torch = self.torch
-        if self.host_launch_s is None:
-            h0 = time.perf_counter()
-            self.replay()
-            self.host_launch_s = time.perf_counter() - h0
-        spin_us = 200.0 + 3.0 * (nrep + 1) * self.host_launch_s * 1e6
-        cycles = int(spin_us * _spin_rate(torch))
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(nrep + 1)]
-        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(self.s):
-            torch.cuda._sleep(cycles)
-            self.g.replay()              # lead-in, untimed
-            ev[0].record(self.s)
-            for i in range(nrep):
-                self.g.replay()
-                ev[i + 1].record(self.s)
+            e0.record(self.s)
+            self.g.replay()
+            e1.record(self.s)
         torch.cuda.synchronize()
-        return [ev[i].elapsed_time(ev[i + 1]) for i in range(nrep)]
+        self.gpu_s = max(e0.elapsed_time(e1) * 1e-3, 1e-6)
+        return done + self.ncalls
 
 
-def time_calls(torch, calls, steps, warmup, replays=0, ncalls=None):
-    """Pre-roll, warm up, then time exactly `steps` calls (one graph replay), and
-    `replays` further replays. Returns a dict with us per call of the timed
-    replay, the replays' spread and the pre-roll count."""
+def time_calls(torch, calls, steps, warmup, replays=0, ncalls=None, preroll=(PREROLL_CALLS, PREROLL_SECONDS)):
+    """Pre-roll, warm up, then time exactly `ncalls` (default `steps`) calls, and
+    `replays` further blocks of as many calls, each block between two HIP events.
+
+    The timed calls are ordinary eager calls of the entry point on one stream.
+    Before each block the stream gets untimed filler -- replays of a graph of
+    the same calls -- long enough (twice the host's time to issue the block)
+    that the host has queued the whole block before the GPU reaches its first
+    event: the events see back-to-back execution only, with no host launch gap
+    and no per-graph launch cost inside. Returns us per call of the first block,
+    the spread of the others and the pre-roll count."""
     ncalls = steps if ncalls is None else ncalls
-    g = Graph(torch, calls, ncalls)
-    pre = g.preroll()
-    if warmup > 0:
-        if warmup % ncalls == 0:
-            g.replay(warmup // ncalls)
-        else:
-            gw = Graph(torch, calls, warmup)
-            gw.replay()
-            del gw
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = Graph(torch, calls, min(max(ncalls, 64), 512), s)
+    pre = g.preroll(*preroll)
+    # warm-up: eager calls, whose host time per call sizes the filler
+    host = []
+    for i in range(max(warmup, 16)):
+        h0 = time.perf_counter()
+        calls[i % len(calls)](s)
+        host.append(time.perf_counter() - h0)
+        if i % 64 == 63:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    ms = g.timed(1 + replays)
-    us = [m * 1000.0 / ncalls for m in ms]
-    out = {"us_per_call": us[0], "preroll_calls": pre, "calls_per_graph": ncalls,
-           "host_launch_us": round(g.host_launch_s * 1e6, 1)}
+    h_call = statistics.median(host)
+    nfill = max(1, -(-int((2.0 * ncalls * h_call + 200e-6) * 1e6) // int(g.gpu_s * 1e6)))
+    blocks = []
+    with torch.cuda.stream(s):
+        for b in range(1 + replays):
+            g.replay(nfill)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for i in range(ncalls):
+                calls[(b * ncalls + i) % len(calls)](s)
+            e1.record(s)
+            blocks.append((e0, e1))
+    torch.cuda.synchronize()
+    us = [a.elapsed_time(z) * 1000.0 / ncalls for a, z in blocks]
+    out = {"us_per_call": us[0], "preroll_calls": pre, "warmup_calls": max(warmup, 16), "calls_per_block": ncalls,
+           "host_us_per_call": round(h_call * 1e6, 1), "filler_calls": nfill * g.ncalls}
     if replays:
         r = sorted(us[1:])
         out["replays"] = {"n": len(r), "median_us": round(statistics.median(r), 3), "min_us": round(r[0], 3),
                           "max_us": round(r[-1], 3)}
     del g
     return out
+
+
+def time_graph_calls(torch, calls, ncalls, nrep=5, preroll=(PREROLL_CALLS, PREROLL_SECONDS)):
+    """us per call inside HIP graphs: a graph of `ncalls` calls (cycling through
+    `calls`) is pre-rolled, then replayed nrep times back to back with a HIP
+    event after each replay; returns the median and the least us per call over
+    the replays. For everything but the headline: graphs keep the host's cost
+    per call (tens of us through Python) out of the GPU's way even for calls of
+    a few microseconds, and a graph of many calls amortises the graph's own
+    launch cost."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = Graph(torch, calls, ncalls, s)
+    g.preroll(*preroll)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nrep + 1)]
+    with torch.cuda.stream(s):
+        g.g.replay()  # lead-in, untimed
+        ev[0].record(s)
+        for i in range(nrep):
+            g.g.replay()
+            ev[i + 1].record(s)
+    torch.cuda.synchronize()
+    us = sorted(ev[i].elapsed_time(ev[i + 1]) * 1000.0 / ncalls for i in range(nrep))
+    del g
+    return statistics.median(us), us[0]
 
 
 # ---- workloads ------------------------------------------------------------
@@ -302,14 +325,15 @@ def nsets_for(wl, ncalls) -> int:
 
 
 def calls_for(wl, steps) -> int:
-    """Calls per graph for a workload timed beside the headline: at least `steps`,
+    """Timed calls for a workload timed beside the headline: at least `steps`,
     and for small workloads enough to touch ROTATE_BYTES of distinct data (capped)."""
     set_bytes = (wl.R + 3) * wl.M * wl.H * wl.esize
-    return max(steps, min(MAX_GRAPH_CALLS, -(-ROTATE_BYTES // set_bytes)))
+    return max(steps, min(MAX_TIMED_CALLS, -(-ROTATE_BYTES // set_bytes)))
 
 
 def time_workload(torch, arrms, wl, paths, steps, warmup, sets=None):
-    """us/call of a workload on each of `paths` over rotating buffer sets."""
+    """us/call of a workload on each of `paths` over rotating buffer sets, inside
+    graphs (time_graph_calls)."""
     ncalls = calls_for(wl, steps)
     own = sets is None
     if own:
@@ -322,9 +346,8 @@ def time_workload(torch, arrms, wl, paths, steps, warmup, sets=None):
     pf = {"one": arrms.FORCE_ONE_STAGE, "two": arrms.FORCE_TWO_STAGE}
     for p in paths:
         calls = [lambda st, d=d: call(arrms, wl, d, wl.flags | pf[p], st) for d in sets.sets]
-        t = time_calls(torch, calls, steps, warmup, ncalls=ncalls)
-        us = t["us_per_call"]
-        r = {"us_per_call": round(us, 3)}
+        us, us_min = time_graph_calls(torch, calls, ncalls, preroll=(PREROLL_CALLS, 0.2))
+        r = {"us_per_call": round(us, 3), "min_us": round(us_min, 3)}
         if bw:
             r["metric_gbs"] = round(metric_bytes_of(wl) / (us * 1e-6) / 1e9, 1)
             r["achieved_gbs"] = round(algo_bytes_of(wl) / (us * 1e-6) / 1e9, 1)
@@ -384,9 +407,9 @@ def time_strided(torch, arrms, wl, pad, steps, warmup):
                                   flags=wl.flags | arrms.FORCE_ONE_STAGE, stream=st)
 
     calls = [lambda st, d=d: one(d, st) for d in sets]
-    t = time_calls(torch, calls, steps, warmup)
+    us, _ = time_graph_calls(torch, calls, max(steps, 64))
     del sets
-    return t["us_per_call"]
+    return us
 
 
 def time_quant(torch, arrms, wl, quant, steps, warmup):
@@ -418,14 +441,15 @@ def time_quant(torch, arrms, wl, quant, steps, warmup):
         arrms.arrms_fused_quant(d["xs"], d["res"], d["w"], None, d["rout"], d["q"], d["s"], eps=wl.eps,
                                 flags=flags, quant=quant, M=M, H=H, stream=st)
 
-    t = time_calls(torch, [lambda st, d=d: one(d, st) for d in sets], steps, warmup)
+    us, _ = time_graph_calls(torch, [lambda st, d=d: one(d, st) for d in sets], max(steps, 64))
     del sets
-    return t["us_per_call"], algo
+    return us, algo
 
 
-def time_sum(torch, arrms, case, R, steps, warmup):
+def time_sum(torch, arrms, case, R, steps, warmup, standalone=False):
     """The plain rank all-reduce on one message over rotating buffer sets.
-    Returns (us per call, algorithmic bytes per call)."""
+    Returns (us per call, algorithmic bytes per call): exactly `steps` eager calls
+    when it is the line's own measurement (standalone), else inside graphs."""
     from all_reduce_residual_rank_amd import workloads as wlmod
     dev = torch.device("cuda")
     xs = wlmod.make_sum_inputs(R, case.numel, 0, case.dtype)
@@ -435,18 +459,19 @@ def time_sum(torch, arrms, case, R, steps, warmup):
             for _ in range(nsets)]
     flags = wlmod.DT_CODE[case.dtype]
     calls = [lambda st, d=d: arrms.arrms_allreduce_sum(d[0], d[1], flags=flags, stream=st) for d in sets]
-    t = time_calls(torch, calls, steps, warmup)
+    if standalone:
+        us = time_calls(torch, calls, steps, warmup)["us_per_call"]
+    else:
+        us, _ = time_graph_calls(torch, calls, max(steps, 64))
     del sets
-    return t["us_per_call"], (R + 1) * case.nbytes
+    return us, (R + 1) * case.nbytes
 
 
 def time_hot(torch, arrms, wl, sets, flags, reps=64):
-    """Single buffer set replayed: cache-resident ("hot") context number."""
-    g = Graph(torch, [lambda st: call(arrms, wl, sets.sets[0], flags, st)], reps)
-    g.preroll(min_calls=reps * 8, min_seconds=0.0)
-    ms = g.timed(5)
-    del g
-    return min(ms) * 1000.0 / reps
+    """Single buffer set, called again and again: cache-resident ("hot") context number."""
+    _, us_min = time_graph_calls(torch, [lambda st: call(arrms, wl, sets.sets[0], flags, st)], reps,
+                                 preroll=(reps * 8, 0.0))
+    return us_min
 
 
 # ---- the data-movement probe (measured ceiling) ---------------------------
@@ -467,7 +492,8 @@ def load_probe():
 def time_probe(torch, lib, wl, sets, steps, warmup, replays):
     """The probe over the workload's own rotating buffers: every row's R + 1 input
     streams read and two output streams written (residual_out and out), in the
-    fused kernel's launch shape and load window, with no arithmetic."""
+    fused kernel's launch shape and load window, with no arithmetic; timed inside
+    graphs (time_graph_calls)."""
     from all_reduce_residual_rank_amd import arrms
     P = wl.H * wl.esize // 16
     ppt = 4 if P % 4 == 0 and P // 4 <= 512 else 2
@@ -483,9 +509,114 @@ def time_probe(torch, lib, wl, sets, steps, warmup, replays):
             raise RuntimeError(f"probe_rows failed: {rc}")
 
     calls = [lambda st, d=d: one(d, st) for d in sets.sets]
-    t = time_calls(torch, calls, steps, warmup, replays=replays)
-    t["launch"] = {"packs_per_thread": ppt, "threads_per_row": tpr, "load_window": 2}
-    return t
+    us, us_min = time_graph_calls(torch, calls, max(steps, 64))
+    return {"us_per_call": us, "min_us": us_min,
+            "launch": {"packs_per_thread": ppt, "threads_per_row": tpr, "load_window": 2}}
+
+
+# ---- launch-shape sweep ---------------------------------------------------
+
+SWEEP_KINDS = {
+    # name: (dtype, flags without the dtype, quant output, what)
+    "bf16": ("bf16", 0, False, "bf16, plain weights, T output"),
+    "fp16_fp8": ("fp16", 4 | 8, True, "fp16, gemma_norm, per-token FP8 without the T mirror"),
+}
+SWEEP_FIELDS = ("kind", "R", "M", "H", "variant", "path", "ppt", "tpr", "window", "us_median", "us_min",
+                "calls_per_graph", "footprint_bytes", "auto_path", "auto_ppt", "auto_tpr", "auto_window",
+                "auto_cap16", "blocks_per_cu", "cus")
+
+
+def sweep(args):
+    """Every valid one-stage launch shape (packs per thread 1-4, each load
+    window), the two-stage path and the automatic choice, per point of the
+    grid; median over 3 replays of a graph of n calls each (time_graph_calls,
+    with a short pre-roll per variant after a long one for the process)."""
+    import csv
+    import math
+    import torch
+    from all_reduce_residual_rank_amd import arrms
+    from all_reduce_residual_rank_amd import workloads as wlmod
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    arrms.arrms_reserve_staging(0)
+    Ms = [int(x) for x in args.sweep_m.split(",")]
+    Hs = [int(x) for x in args.sweep_h.split(",")]
+    Rs = [int(x) for x in args.sweep_r.split(",")]
+    kinds = args.sweep_kinds.split(",")
+    os.makedirs(os.path.dirname(os.path.abspath(args.sweep_out)), exist_ok=True)
+    f = open(args.sweep_out, "w", newline="")
+    wr = csv.DictWriter(f, fieldnames=SWEEP_FIELDS)
+    wr.writeheader()
+    gen = torch.Generator(device=dev)
+    warmed = False
+    t_start = time.perf_counter()
+    for kind in kinds:
+        dtype, kflags, quant, _ = SWEEP_KINDS[kind]
+        T = wlmod.DTYPES[dtype]
+        e = 4 if dtype == "fp32" else 2
+        base_flags = wlmod.DT_CODE[dtype] | kflags
+        for R in Rs:
+            for H in Hs:
+                P = H * e // 16
+                for M in Ms:
+                    gen.manual_seed(M * 131 + H * 7 + R)
+                    algo = (R + 2) * M * H * e + H * e + (M * H + M * 4 if quant else M * H * e)
+                    est_us = max(3.0, algo / 5.5e12 * 1e6)
+                    n = max(64, min(512, math.ceil(1000.0 / est_us)))
+                    set_bytes = (R + 3) * M * H * e
+                    nsets = max(2, min(n, -(-ROTATE_BYTES // set_bytes)))
+                    sets = []
+                    for _ in range(nsets):
+                        d = {"xs": [torch.randn(M, H, generator=gen, device=dev).to(T) for _ in range(R)],
+                             "res": torch.randn(M, H, generator=gen, device=dev).to(T),
+                             "w": (torch.randn(H, generator=gen, device=dev) * 0.1).to(T),
+                             "rout": torch.empty(M, H, dtype=T, device=dev),
+                             "out": None if quant else torch.empty(M, H, dtype=T, device=dev),
+                             "q": torch.empty(M, H, dtype=torch.uint8, device=dev) if quant else None,
+                             "sc": torch.empty(M, dtype=torch.float32, device=dev) if quant else None}
+                        sets.append(d)
+                    auto = arrms.arrms_query_launch(M, H, R, base_flags)
+                    variants = [("auto", 0, 0, 0, 0), ("two", arrms.FORCE_TWO_STAGE, 0, 0, 0)]
+                    for ppt in (1, 2, 3, 4):
+                        tpr = -(-P // ppt)
+                        tpr = -(-tpr // 64) * 64
+                        if tpr > (1024 if (ppt == 1 or dtype == "fp32") else 512):
+                            continue
+                        for win in (1, 2, 3):
+                            if win == 3 and (R + 1) * ppt <= 8:
+                                continue  # the medium window is the wide one for such rows
+                            variants.append((f"ppt{ppt}_w{win}", arrms.FORCE_ONE_STAGE, ppt, tpr, win))
+                    for name, force, ppt, tpr, win in variants:
+                        def mk(d, force=force, ppt=ppt, win=win):
+                            return lambda st: arrms.arrms_fused_config(
+                                d["xs"], d["res"], d["w"], d["out"], d["rout"], d["q"], d["sc"], eps=1e-6,
+                                flags=base_flags | force, ppt=ppt, load_window=win, M=M, H=H, stream=st)
+                        calls = [mk(d) for d in sets]
+                        pre = (PREROLL_CALLS, PREROLL_SECONDS) if not warmed else (n, 0.01)
+                        warmed = True
+                        med, least = time_graph_calls(torch, calls, n, nrep=3, preroll=pre)
+                        if name == "auto":
+                            path = "one" if auto["path"] == 1 else "two"
+                            ppt_r, tpr_r, win_r = auto["ppt"], auto["tpr"], auto["window"]
+                        elif name == "two":
+                            path, ppt_r, tpr_r, win_r = "two", 0, 0, 0
+                        else:
+                            path, ppt_r, tpr_r, win_r = "one", ppt, tpr, win
+                        wr.writerow({"kind": kind, "R": R, "M": M, "H": H, "variant": name, "path": path,
+                                     "ppt": ppt_r, "tpr": tpr_r, "window": win_r,
+                                     "us_median": round(med, 3), "us_min": round(least, 3),
+                                     "calls_per_graph": n, "footprint_bytes": min(n, nsets) * set_bytes,
+                                     "auto_path": auto["path"], "auto_ppt": auto["ppt"], "auto_tpr": auto["tpr"],
+                                     "auto_window": auto["window"], "auto_cap16": auto["cap16"],
+                                     "blocks_per_cu": auto["blocks_per_cu"], "cus": auto["cus"]})
+                    f.flush()
+                    print(f"sweep {kind} R={R} H={H} M={M}: {len(variants)} variants, "
+                          f"{time.perf_counter() - t_start:.0f} s", flush=True)
+                    del sets
+                    torch.cuda.empty_cache()
+    f.close()
+    print(json.dumps({"sweep": args.sweep_out, "seconds": round(time.perf_counter() - t_start, 1)}), flush=True)
 
 
 # ---- host facts -----------------------------------------------------------
@@ -594,6 +725,9 @@ def main():
         print(json.dumps({"error": "the benchmark measures one GPU's share of the collective; run with --gpus 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.sweep:
+        sweep(args)
+        return
     import torch
     from all_reduce_residual_rank_amd import arrms
     from all_reduce_residual_rank_amd import workloads as wlmod
@@ -610,7 +744,7 @@ def main():
     digest = sources_digest()
     if args.sum_only:
         case = wlmod.SUM_HEADLINE
-        us, nbytes = time_sum(torch, arrms, case, 4, args.steps, args.warmup)
+        us, nbytes = time_sum(torch, arrms, case, 4, args.steps, args.warmup, standalone=True)
         gbs = nbytes / (us * 1e-6) / 1e9
         print(json.dumps({
             "metric": "µs/call and achieved HBM GB/s of the plain rank all-reduce, R=4",
@@ -655,7 +789,7 @@ def main():
             other[p] = round(us, 3)
         elif not args.no_other_path:
             c2 = [lambda st, d=d: call(arrms, wl, d, wl.flags | path_flags[p], st) for d in sets.sets]
-            other[p] = round(time_calls(torch, c2, args.steps, args.warmup, ncalls=ncalls)["us_per_call"], 3)
+            other[p] = round(time_calls(torch, c2, args.steps, args.warmup)["us_per_call"], 3)
     hot = None if args.no_hot else time_hot(torch, arrms, wl, sets, wl.flags | path_flags[chosen])
     traffic = load_traffic(wl.name, chosen, digest)
 
@@ -669,9 +803,9 @@ def main():
                    "compute": "fp32 rank sums, fp64 row statistics"},
         "us_per_call": round(us, 3), "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
         "metric_bytes": metric_bytes,
-        "preroll_calls": t["preroll_calls"],
-        "timing": "HIP events around exactly `steps` back-to-back calls of one graph replay, queued behind a GPU "
-                  "spin and an untimed lead-in replay (no host launch gap inside); after the pre-roll and warm-up",
+        "preroll_calls": t["preroll_calls"], "warmup_calls": t["warmup_calls"],
+        "timing": "HIP events around exactly `steps` eager back-to-back calls, queued behind untimed filler work "
+                  "so that no host launch gap falls inside; after the pre-roll and warm-up",
         "path_us": other, "hot_us_cache_resident": None if hot is None else round(hot, 3),
         "replays": t.get("replays"),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,
@@ -687,11 +821,16 @@ def main():
         if lib is not None:
             pt = time_probe(torch, lib, wl, sets, args.steps, args.warmup, args.replays)
             pu = pt["us_per_call"]
+            # the kernel timed the same way as the probe (inside graphs)
+            kcalls = [lambda st, d=d: call(arrms, wl, d, wl.flags | path_flags[chosen], st) for d in sets.sets]
+            ku, ku_min = time_graph_calls(torch, kcalls, max(args.steps, 64))
+            line["graph_us_per_call"] = round(ku, 3)
             line["probe"] = {"kind": "data movement only: R+1 input and 2 output streams per row, no arithmetic",
-                             "us_per_call": round(pu, 3), "replays": pt.get("replays"),
-                             "achieved": round(algo_bytes / (pu * 1e-6) / 1e9, 2), **pt["launch"]}
+                             "us_per_call": round(pu, 3), "min_us": round(pt["min_us"], 3),
+                             "achieved": round(algo_bytes / (pu * 1e-6) / 1e9, 2), **pt["launch"],
+                             "timing": "inside graphs, like graph_us_per_call"}
             line["probe_us"] = round(pu, 3)
-            line["frac_of_probe"] = round(pu / us, 4)
+            line["frac_of_probe"] = round(pu / ku, 4)
     del sets
     torch.cuda.empty_cache()
     if not args.no_workloads:

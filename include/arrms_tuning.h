@@ -41,6 +41,31 @@ ARRMS_API int arrms_fused_config(const void *const *rank_in, int R, const void *
                                  int tpr, int rows_per_block, int blocks, int load_window,
                                  hipStream_t stream);
 
+/*
+ * The row-kernel launch arrms_fused (arrms_fused_quant for quant != 0) makes
+ * for these sizes: the one-stage launch, or the two-stage path's row pass over
+ * its first chunk (with the default staging size). Written to info[0 ..
+ * ARRMS_LAUNCH_INFO - 1]:
+ *   [0] path (ARRMS_PATH_*)     [1] packs per thread   [2] threads per row
+ *   [3] rows per block          [4] load window (1 narrow, 2 wide, 3 medium)
+ *   [5] occupancy cap (1: at most 16 waves per compute unit)
+ *   [6] blocks of this shape (narrow-window kernel) one compute unit holds
+ *   [7] compute units
+ * flags: ARRMS_DTYPE_* | ARRMS_GEMMA | ARRMS_FORCE_* (ARRMS_FP8 means quant =
+ * ARRMS_QUANT_FP8_TOKEN); quant: 0 (T output) or ARRMS_QUANT_*; mirror: the T
+ * mirror of a quantised output is written. Returns ARRMS_OK or the status
+ * arrms_query_path (or arrms_fused_quant's group checks) would give.
+ *
+ * arrms_query_launch asks the current device for [6] and [7] (its occupancy
+ * for each kernel and its compute units). arrms_plan_launch takes them as
+ * arguments and touches no device: pure host code, the same rules, for
+ * checking them against recorded measurements.
+ */
+#define ARRMS_LAUNCH_INFO 8
+ARRMS_API int arrms_query_launch(int M, int H, int R, int flags, int quant, int mirror, int *info);
+ARRMS_API int arrms_plan_launch(int M, int H, int R, int flags, int quant, int mirror, int blocks_per_cu,
+                                int cus, int *info);
+
 #ifdef __cplusplus
 }
 #endif

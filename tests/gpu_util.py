@@ -87,8 +87,20 @@ def _e4m3_mag(codes: np.ndarray) -> np.ndarray:
     return (codes & 0x7F).astype(np.int64)
 
 
-def compare(got: dict, want: dict, dtype: str, *, require_exact_out: bool = True, label: str = ""):
-    """Assert the acceptance bars; returns a small report dict."""
+# fp32 outputs: the squares of fp32 values carry 48 significant bits, so the fp64
+# sum of a row's squares is not exact and its value depends on the summation
+# order (the kernel's tree against the oracle's left-to-right sum): rstd then
+# differs in its last bits and an element within ~1e-14 relative of an fp32
+# rounding boundary may round the other way -- within the 1-ulp bar. For
+# bf16/fp16 the boundaries are 2^16 / 2^13 times wider and no case has shown a
+# difference, so exact bits stay required there. At most this fraction of fp32
+# outputs (and at least one) may take the 1-ulp allowance.
+FP32_ULP_FRAC = 1e-6
+
+
+def compare(got: dict, want: dict, dtype: str, *, require_exact_out: bool | None = None, label: str = ""):
+    """Assert the acceptance bars; returns a small report dict. require_exact_out:
+    None = exact bits for bf16/fp16 and the counted 1-ulp allowance for fp32."""
     rep = {}
     assert np.array_equal(got["residual_out"], want["residual_out"]), \
         f"{label}: residual_out differs in {(got['residual_out'] != want['residual_out']).sum()} elements"
@@ -100,7 +112,11 @@ def compare(got: dict, want: dict, dtype: str, *, require_exact_out: bool = True
             gv, wv = _values(g, dtype), _values(w, dtype)
             bad = ~same & ~(np.abs(gv - wv) <= _ulp_bound(wv, dtype))
             assert not bad.any(), f"{label}: {bad.sum()} outputs beyond 1 ulp"
-            assert not require_exact_out, f"{label}: {(~same).sum()} outputs differ by 1 ulp"
+            if require_exact_out is None and dtype == "fp32":
+                limit = max(1, int(FP32_ULP_FRAC * same.size))
+                assert (~same).sum() <= limit, f"{label}: {(~same).sum()} fp32 outputs differ by 1 ulp (> {limit})"
+            else:
+                assert require_exact_out is False, f"{label}: {(~same).sum()} outputs differ by 1 ulp"
     if want["fp8"] is not None:
         gs, ws = got["scale"], want["scale"]
         rel = np.abs(gs.astype(np.float64) - ws) / np.maximum(np.abs(ws.astype(np.float64)), 1e-300)

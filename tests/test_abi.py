@@ -67,16 +67,16 @@ def test_status_strings():
     assert arrms.arrms_status_string(7) == "unknown status"
 
 
-def _call(R=4, M=8, H=64, flags=0, eps=1e-6, **over):
+def _call(R=4, M=8, H=64, flags=0, eps=1e-6, entry=None, **over):
     ptr = {f"in{r}": BASE + (r if r < 8 else 16) * STRIDE for r in range(9)}
     ptr.update(residual=BASE + 10 * STRIDE, weight=BASE + 11 * STRIDE, out=BASE + 12 * STRIDE,
                residual_out=BASE + 13 * STRIDE, fp8_out=BASE + 14 * STRIDE,
                fp8_scale=BASE + 15 * STRIDE)
     ptr.update(over)
     rank_in = [ptr[f"in{r}"] for r in range(R)]
-    return arrms.arrms_fused_raw(rank_in, R, ptr["residual"], ptr["weight"], ptr["out"],
-                                 ptr["residual_out"], ptr["fp8_out"], ptr["fp8_scale"], M, H, eps,
-                                 flags, None)
+    fn = entry or arrms.arrms_fused_raw
+    return fn(rank_in, R, ptr["residual"], ptr["weight"], ptr["out"], ptr["residual_out"], ptr["fp8_out"],
+              ptr["fp8_scale"], M, H, eps, flags, None)
 
 
 def test_zero_rows_is_ok_and_launches_nothing():
