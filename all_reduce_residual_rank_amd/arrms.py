@@ -48,7 +48,9 @@ QUANT_FP8_TOKEN, QUANT_FP8_GROUP, QUANT_MXFP4 = 1, 2, 3
 FP8_GROUP_SIZE = 128
 MX_BLOCK = 32
 
-EXPORTS = ("arrms_fused", "arrms_fused_strided", "arrms_fused_quant", "arrms_allreduce_sum",
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+EXPORTS = ("arrms_fused", "arrms_fused_noalloc", "arrms_fused_strided", "arrms_fused_quant", "arrms_allreduce_sum",
            "arrms_fused_config", "arrms_query_launch", "arrms_plan_launch",
            "arrms_reserve_staging", "arrms_release_staging", "arrms_staging_bytes", "arrms_query_path",
            "arrms_status_string")
@@ -57,6 +59,8 @@ _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_
 _ll = ctypes.c_longlong
 _lib.arrms_fused.argtypes = [ctypes.POINTER(_vp), _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _vp]
 _lib.arrms_fused.restype = _i
+_lib.arrms_fused_noalloc.argtypes = [ctypes.POINTER(_vp), _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _f, _i, _vp]
+_lib.arrms_fused_noalloc.restype = _i
 _lib.arrms_fused_strided.argtypes = [ctypes.POINTER(_vp), _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
                                      _ll, _ll, _ll, _ll, _ll, _f, _i, _vp]
 _lib.arrms_fused_strided.restype = _i
@@ -217,6 +221,29 @@ def arrms_fused(rank_in, residual, weight, out, residual_out, fp8_out=None, fp8_
                          fp8_scale, M, H, eps, flags, st)
     if rc != OK:
         raise ArrmsError(rc, "arrms_fused")
+
+
+def arrms_fused_noalloc_raw(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale,
+                            M, H, eps, flags, stream) -> int:
+    """arrms_fused_noalloc with addresses as ints; returns the status unchanged."""
+    ptrs = (_vp * max(len(rank_in), 1))(*[_addr(p) for p in rank_in])
+    return _lib.arrms_fused_noalloc(ptrs, int(R), _addr(residual), _addr(weight), _addr(out),
+                                    _addr(residual_out), _addr(fp8_out), _addr(fp8_scale), int(M), int(H),
+                                    float(eps), int(flags), stream)
+
+
+def arrms_fused_noalloc(rank_in, residual, weight, out, residual_out, fp8_out=None, fp8_scale=None, *,
+                        eps: float, flags: int, M: int | None = None, H: int | None = None,
+                        stream=None) -> None:
+    """arrms_fused that never allocates: the two-stage path stages through the
+    library's fixed per-GPU region (calls on one GPU share it)."""
+    if M is None or H is None:
+        M, H = residual.shape[-2], residual.shape[-1]
+    _check_fused(rank_in, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H, flags)
+    rc = arrms_fused_noalloc_raw(rank_in, len(rank_in), residual, weight, out, residual_out, fp8_out,
+                                 fp8_scale, M, H, eps, flags, _stream_handle(stream))
+    if rc != OK:
+        raise ArrmsError(rc, "arrms_fused_noalloc")
 
 
 def arrms_fused_strided_raw(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale,

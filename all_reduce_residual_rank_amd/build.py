@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libarrms.so")
 
 SOURCES = ["kern_bf16_t.hip", "kern_bf16_fp8.hip", "kern_bf16_fp8t.hip", "kern_fp16_t.hip",
            "kern_fp16_fp8.hip", "kern_fp16_fp8t.hip", "kern_fp32_t.hip", "kern_bf16_fp8g.hip",
-           "kern_bf16_mx4.hip", "kern_fp16_fp8g.hip", "kern_fp16_mx4.hip", "api.cpp"]
+           "kern_bf16_mx4.hip", "kern_fp16_fp8g.hip", "kern_fp16_mx4.hip", "api.cpp", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: keep the compiler from forming packed fp32 arithmetic;

@@ -529,7 +529,7 @@ bool apply_shape(const ShapeReq *req, int P, int R, long long M, bool fp32, arrm
 int fused_impl(const void *const *rank_in, int R, const void *residual, const void *weight,
                void *out, void *residual_out, void *fp8_out, void *fp8_scale, int M, int H,
                float eps, int flags, const Strides &ld, const ShapeReq *req, hipStream_t stream,
-               int quant)
+               int quant, void *fixed_staging = nullptr, size_t fixed_staging_bytes = 0)
 {
     int rc = validate(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H,
                       eps, flags, ld, quant);
@@ -581,10 +581,12 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
     }
 
     // ---- two-stage: per row chunk, flat rank reduce into staging, then the
-    // row pass with the staging rows as its single input.
-    void *staging;
-    size_t staging_bytes;
-    {
+    // row pass with the staging rows as its single input. The staging is the
+    // library's buffer of the current device, or the caller's fixed region
+    // (which never allocates).
+    void *staging = fixed_staging;
+    size_t staging_bytes = fixed_staging_bytes;
+    if (!fixed_staging) {
         int dev;
         rc = current_device(&dev);
         if (rc != ARRMS_OK)
@@ -608,7 +610,7 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
     const size_t row_bytes = (size_t)H * (size_t)e;
     const long long cap = (long long)(staging_bytes / row_bytes);  // rows the staging holds
     if (cap < 1)
-        return ARRMS_ERR_NO_STAGING;
+        return fixed_staging ? ARRMS_ERR_UNSUPPORTED : ARRMS_ERR_NO_STAGING;
     // chunks of equal size (at most cap rows each): no small last chunk, whose
     // two launches would run a short, latency-bound round of blocks
     const long long nchunks = (M + cap - 1) / cap;
@@ -661,6 +663,28 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
 }
 
 }  // namespace
+
+namespace arrms {
+
+int fused_validate(const void *const *rank_in, int R, const void *residual, const void *weight, const void *out,
+                   const void *residual_out, const void *fp8_out, const float *fp8_scale, int M, int H, float eps,
+                   int flags)
+{
+    const Strides ld = {H, H, H, H, H};
+    return validate(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H, eps, flags, ld,
+                    (flags & ARRMS_FP8) ? Q_TOKEN : Q_NONE);
+}
+
+int fused_fixed_staging(const void *const *rank_in, int R, const void *residual, const void *weight, void *out,
+                        void *residual_out, void *fp8_out, float *fp8_scale, int M, int H, float eps, int flags,
+                        void *staging, size_t staging_bytes, hipStream_t stream)
+{
+    const Strides ld = {H, H, H, H, H};
+    return fused_impl(rank_in, R, residual, weight, out, residual_out, fp8_out, fp8_scale, M, H, eps, flags, ld,
+                      nullptr, stream, (flags & ARRMS_FP8) ? Q_TOKEN : Q_NONE, staging, staging_bytes);
+}
+
+}  // namespace arrms
 
 extern "C" {
 

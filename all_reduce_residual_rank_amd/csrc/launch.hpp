@@ -91,6 +91,17 @@ hipError_t launch_row_bf16_fp8g(const RowArgs &a, int R, const RowShape &s, hipS
 hipError_t launch_row_bf16_mx4(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
 hipError_t launch_row_fp16_fp8g(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
 hipError_t launch_row_fp16_mx4(const RowArgs &a, int R, const RowShape &s, hipStream_t st);
+// The argument checks of arrms_fused alone (api.cpp): ARRMS_OK or its error status.
+int fused_validate(const void *const *rank_in, int R, const void *residual, const void *weight, const void *out,
+                   const void *residual_out, const void *fp8_out, const float *fp8_scale, int M, int H, float eps,
+                   int flags);
+
+// arrms_fused with a caller-provided staging region for the two-stage path
+// (api.cpp): nothing is allocated; rows are chunked to fit staging_bytes.
+int fused_fixed_staging(const void *const *rank_in, int R, const void *residual, const void *weight, void *out,
+                        void *residual_out, void *fp8_out, float *fp8_scale, int M, int H, float eps, int flags,
+                        void *staging, size_t staging_bytes, hipStream_t stream);
+
 // Blocks of the row kernel of that shape (its tpr * rpb threads and its load
 // window) that one compute unit of the current device holds; 0 if the runtime
 // cannot tell. Cached per device.

@@ -61,6 +61,7 @@ extern "C" {
 #define ARRMS_MAX_HIDDEN 16384
 #define ARRMS_MAX_ROW_BYTES 65536 /* H * sizeof(T): bf16/fp16 rows up to 32 KiB, fp32 up to 64 KiB */
 #define ARRMS_DEFAULT_STAGING_BYTES (16u << 20) /* 16 MiB staging region (PR #6699 Changes) */
+#define ARRMS_NOALLOC_SCRATCH_BYTES (16u << 20) /* fixed staging of arrms_fused_noalloc, per GPU */
 
 /* ---- paths returned by arrms_query_path ---------------------------------- */
 #define ARRMS_PATH_NONE 0          /* M == 0: nothing to launch */
@@ -120,6 +121,30 @@ extern "C" {
 ARRMS_API int arrms_fused(const void *const *rank_in, int R, const void *residual, const void *weight,
                 void *out, void *residual_out, void *fp8_out, float *fp8_scale, int M, int H,
                 float eps, int flags, hipStream_t stream);
+
+/*
+ * arrms_fused_noalloc -- arrms_fused for callers that cannot allocate device
+ * memory: code under HIP graph capture with no staging reserved beforehand,
+ * tight serving loops, harnesses that forbid hipMalloc. Arguments, results,
+ * paths and errors are arrms_fused's; no call allocates or frees anything.
+ *
+ * The two-stage path stages its rows in a fixed region of
+ * ARRMS_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds on every GPU it
+ * runs on until the process ends (rows go through it in chunks that fit; a row
+ * wider than the region would be ARRMS_ERR_UNSUPPORTED, which no H up to
+ * ARRMS_MAX_HIDDEN reaches). The region's address is looked up once per device,
+ * on the first call there with valid arguments and M > 0 (ARRMS_ERR_HIP if
+ * that fails): make that first call outside graph capture. Every call on one GPU
+ * shares the region, and its contents are whatever the last call left (every
+ * byte a call reads there it has written first): two-stage calls that overlap
+ * in time on one GPU -- on different streams, or from different threads --
+ * race on it and must be ordered by the caller. The one-stage path uses no
+ * scratch at all.
+ */
+ARRMS_API int arrms_fused_noalloc(const void *const *rank_in, int R, const void *residual,
+                                  const void *weight, void *out, void *residual_out, void *fp8_out,
+                                  float *fp8_scale, int M, int H, float eps, int flags,
+                                  hipStream_t stream);
 
 /*
  * arrms_fused_strided -- arrms_fused over row-strided (padded) matrices. The

@@ -81,7 +81,21 @@ def _call(R=4, M=8, H=64, flags=0, eps=1e-6, entry=None, **over):
 
 def test_zero_rows_is_ok_and_launches_nothing():
     assert _call(M=0) == arrms.OK
+    assert _call(M=0, entry=arrms.arrms_fused_noalloc_raw) == arrms.OK
     assert arrms.arrms_query_path(0, 6144, 4, 0) == arrms.PATH_NONE
+
+
+@pytest.mark.parametrize("kw", [
+    dict(R=0), dict(R=9), dict(M=-1), dict(H=0), dict(flags=3), dict(flags=1 << 7), dict(eps=-1.0),
+    dict(flags=arrms.FORCE_ONE_STAGE | arrms.FORCE_TWO_STAGE), dict(residual=None), dict(in2=None),
+    dict(flags=arrms.FP8, fp8_scale=None), dict(H=60), dict(H=arrms.MAX_HIDDEN + 8),
+    dict(flags=arrms.DTYPE_FP32 | arrms.FP8), dict(in1=BASE + STRIDE + 8), dict(out=BASE + STRIDE + 16),
+])
+def test_noalloc_checks_arguments_like_arrms_fused(kw):
+    # the no-alloc form runs arrms_fused's argument checks before any device call
+    want = _call(**kw)
+    assert want != arrms.OK
+    assert _call(entry=arrms.arrms_fused_noalloc_raw, **kw) == want
 
 
 @pytest.mark.parametrize("kw", [
