@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <cmath>
 #include <mutex>
 
 #include "arrms.h"
@@ -202,12 +203,16 @@ int choose_path(int M, int H, int R, int flags)
     if (flags & ARRMS_FORCE_ONE_STAGE)
         return ARRMS_PATH_ONE_STAGE;
     // One GPU: the one-stage kernel moves the fewest bytes (R inputs + residual
-    // in, two outputs); two-stage adds a staging write and read.
+    // in, two outputs); two-stage adds a staging write and read. Measured: at
+    // none of the 324 points of the launch-shape sweep (rows 1-4096, hidden
+    // 512-8192, 2/4/8 ranks, bf16 T output and fp16 per-token FP8) is it the
+    // fastest; it takes 1.18 to 2 times the best one-stage launch.
     return ARRMS_PATH_ONE_STAGE;
 }
 
-// Row kernel launch shape: packs per thread (PPT) in 1..4, threads per row
-// tpr = the PPT-covering multiple of 64, at most 512. Exact cover first, then
+// Row kernel launch shape by rule (the fallback of choose_shape below, and the
+// shape of launches the measured table does not cover): packs per thread
+// (PPT) in 1..4, threads per row tpr = the PPT-covering multiple of 64, at most 512. Exact cover first, then
 // least padding, then more packs per thread (fewer, busier threads: measured
 // faster on MI355X for large launches) as long as a thread's R+1 input packs
 // stay within 20 (80 registers). Launches of fewer than 512 rows cap PPT at 2
@@ -215,7 +220,7 @@ int choose_path(int M, int H, int R, int flags)
 // rows of 513 to 1024 packs take one pack per thread (blocks of up to 1024
 // threads), and the FP8 epilogue, with more per-element work after the row
 // reduction, caps PPT at 3.
-arrms::RowShape choose_shape(int P, int R, long long M, bool fp8, bool fp32)
+arrms::RowShape rule_shape(int P, int R, long long M, bool fp8, bool fp32)
 {
     // fp32 kernels take blocks of up to 1024 threads at any PPT (rows of up to
     // 4096 packs); the others at one pack per thread only
@@ -262,6 +267,60 @@ arrms::RowShape choose_shape(int P, int R, long long M, bool fp8, bool fp32)
         return best;
     best.rpb = best.tpr >= 256 ? 1 : 256 / best.tpr;
     return best;
+}
+
+#include "dispatch_table.inc"
+
+// Index of the grid value nearest to v on a log scale.
+template <int N> int nearest_log(const int (&grid)[N], double v)
+{
+    const double lv = std::log2(v);
+    int best = 0;
+    double bd = 1e300;
+    for (int i = 0; i < N; ++i) {
+        const double d = std::fabs(std::log2((double)grid[i]) - lv);
+        if (d < bd) {
+            bd = d;
+            best = i;
+        }
+    }
+    return best;
+}
+
+// The measured launch shape: the dispatch table's entry (dispatch_table.inc,
+// written by gen_dispatch_table.py from the launch-shape sweep that bench.py
+// --sweep records on MI355X, profiles/dispatch_sweep_train.csv) at the grid
+// point nearest to this launch -- kind of call (T output or a quantised
+// output), ranks, packs per row and rows, each on a log scale. ppt == 0 when
+// the entry's packs per thread cannot cover this row in one block.
+arrms::RowShape measured_shape(int P, int R, long long M, bool quant, bool fp32)
+{
+    arrms::RowShape s = {0, 0, 0, false, 0, 0, false};
+    const int v = kTab[quant ? 1 : 0][nearest_log(kTabR, R)][nearest_log(kTabP, P)][nearest_log(kTabM, (double)M)];
+    const int ppt = v & 15, win = v >> 4;
+    const int tpr = ((P + ppt - 1) / ppt + 63) / 64 * 64;
+    if (ppt < 1 || ppt > 4 || win < 1 || win > 3 || tpr > ((ppt == 1 || fp32) ? 1024 : 512))
+        return s;
+    s = {ppt, tpr, tpr >= 256 ? 1 : 256 / tpr, tpr * ppt != P, 0, win, false};
+    return s;
+}
+
+// Launch shape of a row-kernel launch (one-stage, and the two-stage row pass,
+// which takes the one-stage shape of the whole launch so that both paths sum
+// each row's squares in the same order): the measured shape, with its load
+// window -- unless no table entry applies, or the row width is not one of the
+// swept ones and the measured packs per thread would pad this row by more than
+// a sixteenth beyond what the rule shape pads.
+arrms::RowShape choose_shape(int P, int R, long long M, bool quant, bool fp32)
+{
+    const arrms::RowShape r = rule_shape(P, R, M, quant, fp32);
+    const arrms::RowShape m = measured_shape(P, R, M, quant, fp32);
+    if (m.ppt == 0)
+        return r;
+    const bool swept = kTabP[nearest_log(kTabP, P)] == P;
+    if (!swept && r.ppt != 0 && (m.tpr * m.ppt - P) > (r.tpr * r.ppt - P) + P / 16)
+        return r;
+    return m;
 }
 
 hipError_t launch_row(int dt, int quant, bool mirror, const arrms::RowArgs &a, int R,
@@ -499,6 +558,8 @@ bool apply_shape(const ShapeReq *req, int P, int R, long long M, bool fp32, arrm
     (void)M;
     if (!req)
         return true;
+    if (req->ppt || req->tpr)
+        s.window = 0;  // a window measured for another shape does not carry over
     if (req->ppt) {
         if (req->ppt < 1 || req->ppt > 4)
             return false;
@@ -522,7 +583,8 @@ bool apply_shape(const ShapeReq *req, int P, int R, long long M, bool fp32, arrm
     s.grid = req->grid;
     if (req->window < 0 || req->window > 3)
         return false;
-    s.window = req->window;
+    if (req->window)
+        s.window = req->window;
     return true;
 }
 
@@ -652,6 +714,7 @@ int fused_impl(const void *const *rank_in, int R, const void *residual, const vo
         // the row pass takes the one-stage shape of the whole launch, so both paths
         // reduce the row statistics in the same order and give the same bits
         arrms::RowShape s = choose_shape(P, R, M, fp8, dt == DT_FP32);
+        s.window = 0;  // the measured window is the one-stage launch's; the row pass takes the rule's
         if (s.ppt == 0 || !apply_shape(req, P, R, n, dt == DT_FP32, s))
             return ARRMS_ERR_UNSUPPORTED;
         plan_window(s, 1, n, P, resident_blocks(dt, quant, out != nullptr, 1, n, P, s));
@@ -764,6 +827,8 @@ int plan_launch(int M, int H, int R, int flags, int quant, int mirror, int bpc, 
     arrms::RowShape s = choose_shape(P, R, M, q != Q_NONE, dt == DT_FP32);
     if (s.ppt == 0)
         return ARRMS_ERR_UNSUPPORTED;
+    if (path == ARRMS_PATH_TWO_STAGE)
+        s.window = 0;
     long long resident;
     if (bpc < 0) {
         arrms::RowShape n = s;

@@ -104,7 +104,7 @@ def parse():
                    help="time every launch shape, load window and path of the row kernel over a grid of "
                         "rows x hidden x ranks (bf16 T output, fp16 gemma per-token FP8) and write a CSV")
     p.add_argument("--sweep-out", default=os.path.join(ROOT, "profiles", "dispatch_sweep.csv"))
-    p.add_argument("--sweep-m", default="1,16,64,256,1024,2800,4096")
+    p.add_argument("--sweep-m", default="1,16,64,256,512,1024,2048,2800,4096")
     p.add_argument("--sweep-h", default="512,2880,4096,6144,7168,8192")
     p.add_argument("--sweep-r", default="2,4,8")
     p.add_argument("--sweep-kinds", default="bf16,fp16_fp8")
