@@ -108,6 +108,9 @@ def parse():
     p.add_argument("--sweep-h", default="512,2880,4096,6144,7168,8192")
     p.add_argument("--sweep-r", default="2,4,8")
     p.add_argument("--sweep-kinds", default="bf16,fp16_fp8")
+    p.add_argument("--graph", action="store_true",
+                   help="time the chosen workload inside graphs of --steps calls replayed back to back "
+                        "(as every figure but the headline is), e.g. for kernel traces of latency-bound launches")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 256 MiB device-to-device copy (4 times) so that a "
                         "profiler's FETCH_SIZE/WRITE_SIZE can be scaled by a kernel of known size")
@@ -495,23 +498,23 @@ def time_probe(torch, lib, wl, sets, steps, warmup, replays):
     fused kernel's launch shape and load window, with no arithmetic; timed inside
     graphs (time_graph_calls)."""
     from all_reduce_residual_rank_amd import arrms
-    P = wl.H * wl.esize // 16
-    ppt = 4 if P % 4 == 0 and P // 4 <= 512 else 2
-    tpr = -(-P // ppt)
-    tpr = -(-tpr // 64) * 64
+    # the fused kernel's own launch shape and load window for this workload
+    plan = arrms.arrms_query_launch(wl.M, wl.H, wl.R, wl.flags & ~arrms.FP8)
+    ppt, tpr = plan["ppt"], plan["tpr"]
+    window = {1: 2 if wl.R > 1 else 3, 2: 16, 3: 8}[plan["window"]]
     vp = ctypes.c_void_p
 
     def one(d, st):
         ins = (vp * (wl.R + 1))(*[x.data_ptr() for x in d["xs"]], d["res"].data_ptr())
         outs = (vp * 2)(d["rout"].data_ptr(), d["out"].data_ptr())
-        rc = lib.probe_rows(ins, wl.R + 1, outs, 2, wl.M, wl.H * wl.esize, ppt, tpr, 2, st.cuda_stream)
+        rc = lib.probe_rows(ins, wl.R + 1, outs, 2, wl.M, wl.H * wl.esize, ppt, tpr, window, st.cuda_stream)
         if rc != 0:
             raise RuntimeError(f"probe_rows failed: {rc}")
 
     calls = [lambda st, d=d: one(d, st) for d in sets.sets]
     us, us_min = time_graph_calls(torch, calls, max(steps, 64))
     return {"us_per_call": us, "min_us": us_min,
-            "launch": {"packs_per_thread": ppt, "threads_per_row": tpr, "load_window": 2}}
+            "launch": {"packs_per_thread": ppt, "threads_per_row": tpr, "load_window": window}}
 
 
 # ---- launch-shape sweep ---------------------------------------------------
@@ -776,7 +779,12 @@ def main():
         arrms.arrms_query_path(wl.M, wl.H, wl.R, wl.flags)]
     chosen = auto_path if args.path == "auto" else args.path
     calls = [lambda st, d=d: call(arrms, wl, d, wl.flags | path_flags[chosen], st) for d in sets.sets]
-    t = time_calls(torch, calls, args.steps, args.warmup, replays=args.replays, ncalls=ncalls)
+    if args.graph:
+        gu, gmin = time_graph_calls(torch, calls, ncalls, nrep=max(3, args.replays))
+        t = {"us_per_call": gu, "preroll_calls": PREROLL_CALLS, "warmup_calls": 0,
+             "replays": {"n": max(3, args.replays), "median_us": round(gu, 3), "min_us": round(gmin, 3)}}
+    else:
+        t = time_calls(torch, calls, args.steps, args.warmup, replays=args.replays, ncalls=ncalls)
     us = t["us_per_call"]
     metric_bytes = metric_bytes_of(wl)
     algo_bytes = algo_bytes_of(wl)
@@ -804,8 +812,9 @@ def main():
         "us_per_call": round(us, 3), "pct_of_peak": round(100.0 * gbs / PEAK_GBS, 2),
         "metric_bytes": metric_bytes,
         "preroll_calls": t["preroll_calls"], "warmup_calls": t["warmup_calls"],
-        "timing": "HIP events around exactly `steps` eager back-to-back calls, queued behind untimed filler work "
-                  "so that no host launch gap falls inside; after the pre-roll and warm-up",
+        "timing": ("median over replays of a graph of `steps` calls (--graph)" if args.graph else
+                   "HIP events around exactly `steps` eager back-to-back calls, queued behind untimed filler work "
+                   "so that no host launch gap falls inside; after the pre-roll and warm-up"),
         "path_us": other, "hot_us_cache_resident": None if hot is None else round(hot, 3),
         "replays": t.get("replays"),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBS,

@@ -75,6 +75,7 @@ template <int NIN, int PPT> hipError_t go_w(const ProbeArgs &a, long long rows, 
     case 1: return go<NIN, PPT, 1>(a, rows, st);
     case 2: return go<NIN, PPT, 2>(a, rows, st);
     case 3: return go<NIN, PPT, 3>(a, rows, st);
+    case 8: return go<NIN, PPT, 8>(a, rows, st);
     default: return go<NIN, PPT, 16>(a, rows, st);
     }
 }
@@ -94,14 +95,15 @@ template <int NIN> hipError_t go_p(const ProbeArgs &a, long long rows, int ppt, 
 // Returns 0 on success, -1 for arguments it does not take (nothing launched),
 // -4 for a launch error. in: nin device pointers (2..9) to rows x row_bytes;
 // out: nout (= 2) device pointers of the same size; ppt 1..4; tpr a multiple of
-// 64, at most 1024, with tpr * ppt * 16 >= row_bytes; window 1, 2, 3 or 16.
+// 64, at most 1024, with tpr * ppt * 16 >= row_bytes; window 1, 2, 3, 8 or 16.
 extern "C" __attribute__((visibility("default"))) int probe_rows(const void *const *in, int nin, void *const *out,
                                                                  int nout, long long rows, int row_bytes, int ppt,
                                                                  int tpr, int window, hipStream_t st)
 {
     if (nin < 2 || nin > kMaxIn || nout != 2 || rows < 0 || rows > 0x7fffffffLL || row_bytes < 16 ||
         row_bytes % 16 || ppt < 1 || ppt > 4 || tpr < 64 || tpr > 1024 || tpr % 64 ||
-        (long long)tpr * ppt * 16 < row_bytes || (window != 1 && window != 2 && window != 3 && window != 16))
+        (long long)tpr * ppt * 16 < row_bytes ||
+        (window != 1 && window != 2 && window != 3 && window != 8 && window != 16))
         return -1;
     if (rows == 0)
         return 0;

@@ -39,6 +39,27 @@ def kernel_stats(trace_dir):
                 "min_ns": min(v), "max_ns": max(v)} for k, v in by.items()}
 
 
+def last_dispatches(trace_dir, n):
+    """Durations of the last n dispatches of the library's kernels, their mean
+    start-to-start spacing and the idle time between one kernel's end and the
+    next one's start, as markdown lines."""
+    rows = [r for r in _csv(trace_dir, "kernel_trace.csv") if "arrms::" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    rows = rows[-n:]
+    by = {}
+    for r in rows:
+        by.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    st = [int(r["Start_Timestamp"]) for r in rows]
+    en = [int(r["End_Timestamp"]) for r in rows]
+    gaps = [(st[i + 1] - en[i]) / 1e3 for i in range(len(rows) - 1)]
+    out = [f"- `{k[:90]}`: {len(v)} dispatches, mean {statistics.mean(v):.3f} us, median {statistics.median(v):.3f} us"
+           for k, v in by.items()]
+    out.append(f"- start-to-start spacing: mean {(st[-1] - st[0]) / 1e3 / (len(rows) - 1):.3f} us")
+    out.append(f"- idle between one kernel's end and the next one's start: median {statistics.median(gaps):.3f} us, "
+               f"mean {statistics.mean(gaps):.3f} us")
+    return out
+
+
 def counter(dir_, name):
     rows = _csv(dir_, "counter_collection.csv")
     by = {}
@@ -58,8 +79,11 @@ def copy_kernel(names):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--trace", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--fetch", help="rocprofv3 --pmc FETCH_SIZE output (omit for a trace-only summary)")
+    ap.add_argument("--write", help="rocprofv3 --pmc WRITE_SIZE output")
+    ap.add_argument("--last", type=int, default=0,
+                    help="also summarise the last N dispatches of the library's kernels (the timed graph "
+                         "replays): durations, start-to-start spacing, idle gap between kernels")
     ap.add_argument("--workload", required=True)
     ap.add_argument("--path", required=True)
     ap.add_argument("--command", required=True)
@@ -67,12 +91,12 @@ def main():
     ap.add_argument("--algo-bytes", type=int, required=True)
     ap.add_argument("--bench-us", type=float, required=True, help="bench.py us/call of the same command")
     ap.add_argument("--out", required=True)
-    ap.add_argument("--traffic-json", required=True)
+    ap.add_argument("--traffic-json")
     a = ap.parse_args()
 
     ks = kernel_stats(a.trace)
-    fetch = counter(a.fetch, "FETCH_SIZE")
-    write = counter(a.write, "WRITE_SIZE")
+    fetch = counter(a.fetch, "FETCH_SIZE") if a.fetch else {}
+    write = counter(a.write, "WRITE_SIZE") if a.write else {}
     ck = copy_kernel(fetch)
     # the copy may be split into several dispatches: scale by the total over one copy
     f_copy = sum(fetch[ck]) / 4.0 if ck else None
@@ -82,15 +106,23 @@ def main():
     ours = [k for k in ks if "arrms::" in k]
     lines = [f"# rocprofv3 summary: {a.workload}, path {a.path}", "",
              "Command (run from the repository root, one run per block below):", "",
-             "```", f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- {a.command}",
-             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- {a.command}",
-             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- {a.command}", "```", "",
+             "```", f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- {a.command}"] + \
+            ([f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- {a.command}",
+              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- {a.command}"] if a.fetch else []) + \
+            ["```", "",
              f"Kernel sources digest: `{a.digest}`. bench.py us/call of the same command: {a.bench_us:.3f}.",
              "", "| kernel | dispatches | avg us | median us | min us | max us |", "|---|---|---|---|---|---|"]
     for k in sorted(ks, key=lambda k: -ks[k]["avg_ns"] * ks[k]["count"]):
         v = ks[k]
         lines.append(f"| `{k[:90]}` | {v['count']} | {v['avg_ns']/1e3:.3f} | {v['median_ns']/1e3:.3f} | "
                      f"{v['min_ns']/1e3:.3f} | {v['max_ns']/1e3:.3f} |")
+    if a.last:
+        lines += ["", f"The last {a.last} dispatches of the library's kernels (the timed graph replays, calls back "
+                  "to back):", ""] + last_dispatches(a.trace, a.last)
+    if not a.fetch:
+        open(a.out, "w").write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return
     lines += ["", "HBM traffic per dispatch (counter KiB scaled by the 256 MiB copy's reading):", ""]
     if ck:
         lines.append(f"- copy kernel `{ck}`: FETCH_SIZE {f_copy:.0f} KiB, WRITE_SIZE {w_copy:.0f} KiB per "

@@ -299,6 +299,49 @@ def test_two_stage_in_capture_without_staging_is_refused():
     assert arrms.arrms_staging_bytes() == arrms.DEFAULT_STAGING_BYTES
 
 
+def test_graph_survives_staging_growth():
+    # a graph captured on the two-stage path holds the staging address it was
+    # captured with; growing the staging afterwards retires that buffer instead
+    # of freeing it, so the graph keeps replaying correctly (and the eager calls
+    # in between, which take the new buffer, stay correct too)
+    dev = torch.device("cuda")
+    torch.cuda.synchronize()
+    arrms.arrms_release_staging()
+    wl = wlmod.Workload("regrow", R=3, M=64, H=2880, dtype="bf16")
+    arrms.arrms_reserve_staging(9 * 2880 * 2)  # 9 rows: the captured call runs 8 chunks
+    small = arrms.arrms_staging_bytes()
+    xs, res, w = wlmod.make_inputs(wl, seed=41)
+    want = gu.run_oracle(wl, xs, res, w)
+    xd = [x.to(dev) for x in xs]
+    rd, wd = res.to(dev), w.to(dev)
+    out = torch.empty(wl.M, wl.H, dtype=torch.bfloat16, device=dev)
+    rout = torch.empty_like(out)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        arrms.arrms_fused(xd, rd, wd, out, rout, eps=wl.eps, flags=wl.flags | PATHS["two"], stream=s)
+    torch.cuda.synchronize()
+    try:
+        for step in range(3):
+            # grow the staging (a new buffer each time; the old ones are retired)
+            arrms.arrms_reserve_staging(small * (step + 2))
+            assert arrms.arrms_staging_bytes() == small * (step + 2)
+            eager = gu.run_hip(wl, xs, res, w, extra_flags=PATHS["two"])
+            gu.compare(eager, want, wl.dtype, label=f"eager-after-growth-{step}")
+            gu.poison_(out)
+            gu.poison_(rout)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            got = {"out": gu.host_bits(out), "residual_out": gu.host_bits(rout), "fp8": None, "scale": None}
+            gu.compare(got, want, wl.dtype, label=f"replay-after-growth-{step}")
+    finally:
+        del g
+        torch.cuda.synchronize()
+        arrms.arrms_release_staging()
+
+
 def test_small_staging_forces_many_chunks():
     # a staging buffer of a few rows exercises the chunk loop (and its row offsets)
     torch.cuda.synchronize()
