@@ -23,8 +23,10 @@ constexpr int kMaxOut = 2;
 struct ProbeArgs {
     const void *in[kMaxIn];
     void *out[kMaxOut];
-    int P;  // packs per row
+    int P;    // packs per row
     int tpr;
+    int bpr;  // blocks per row: block b takes part b % bpr of row b / bpr
+    int part; // packs per part, ceil(P / bpr)
 };
 
 template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
@@ -32,26 +34,29 @@ template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_wai
 template <int NIN, int NOUT, int PPT, int W>
 __global__ void __launch_bounds__(1024) probe_kernel(const ProbeArgs a)
 {
-    const long long row = blockIdx.x;
+    const long long row = blockIdx.x / a.bpr;
+    const int p0 = (int)(blockIdx.x % a.bpr) * a.part;
+    const int pend = p0 + a.part < a.P ? p0 + a.part : a.P;
     const int lt = threadIdx.x;
     u32x4 x[PPT][NIN];
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
-        const int j = lt + k * a.tpr;
+        // packs past this block's part load a pack of the row that exists (the
+        // last one) and are not stored: no branch around the loads, whose
+        // merge would make the compiler wait for each load in turn
+        const int j = p0 + lt + k * a.tpr;
+        const int jc = j < pend ? j : a.P - 1;
 #pragma unroll
         for (int s = 0; s < NIN; ++s) {
-            if (j < a.P)
-                x[k][s] = __builtin_nontemporal_load((const u32x4 *)a.in[s] + row * a.P + j);
-            else
-                x[k][s] = u32x4{0u, 0u, 0u, 0u};
+            x[k][s] = __builtin_nontemporal_load((const u32x4 *)a.in[s] + row * a.P + jc);
             wait_vm<W - 1>();
         }
     }
     wait_vm<0>();
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
-        const int j = lt + k * a.tpr;
-        if (j >= a.P)
+        const int j = p0 + lt + k * a.tpr;
+        if (j >= pend)
             continue;
         u32x4 acc = x[k][0];
 #pragma unroll
@@ -65,7 +70,7 @@ __global__ void __launch_bounds__(1024) probe_kernel(const ProbeArgs a)
 
 template <int NIN, int PPT, int W> hipError_t go(const ProbeArgs &a, long long rows, hipStream_t st)
 {
-    hipLaunchKernelGGL((probe_kernel<NIN, 2, PPT, W>), dim3((unsigned)rows), dim3(a.tpr), 0, st, a);
+    hipLaunchKernelGGL((probe_kernel<NIN, 2, PPT, W>), dim3((unsigned)(rows * a.bpr)), dim3(a.tpr), 0, st, a);
     return hipGetLastError();
 }
 
@@ -94,15 +99,22 @@ template <int NIN> hipError_t go_p(const ProbeArgs &a, long long rows, int ppt, 
 
 // Returns 0 on success, -1 for arguments it does not take (nothing launched),
 // -4 for a launch error. in: nin device pointers (2..9) to rows x row_bytes;
-// out: nout (= 2) device pointers of the same size; ppt 1..4; tpr a multiple of
-// 64, at most 1024, with tpr * ppt * 16 >= row_bytes; window 1, 2, 3, 8 or 16.
-extern "C" __attribute__((visibility("default"))) int probe_rows(const void *const *in, int nin, void *const *out,
-                                                                 int nout, long long rows, int row_bytes, int ppt,
-                                                                 int tpr, int window, hipStream_t st)
+// out: nout (= 2) device pointers of the same size; bpr blocks per row (1..64),
+// each taking ceil(packs / bpr) consecutive packs of its row; ppt 1..4; tpr a
+// multiple of 64, at most 1024, with tpr * ppt covering a block's packs;
+// window 1, 2, 3, 8 or 16.
+extern "C" __attribute__((visibility("default"))) int probe_rows_split(const void *const *in, int nin,
+                                                                       void *const *out, int nout, long long rows,
+                                                                       int row_bytes, int ppt, int tpr, int window,
+                                                                       int bpr, hipStream_t st)
 {
-    if (nin < 2 || nin > kMaxIn || nout != 2 || rows < 0 || rows > 0x7fffffffLL || row_bytes < 16 ||
+    if (bpr < 1 || bpr > 64)
+        return -1;
+    const int P = row_bytes / 16;
+    const int part = (P + bpr - 1) / bpr;
+    if (nin < 2 || nin > kMaxIn || nout != 2 || rows < 0 || rows * bpr > 0x7fffffffLL || row_bytes < 16 ||
         row_bytes % 16 || ppt < 1 || ppt > 4 || tpr < 64 || tpr > 1024 || tpr % 64 ||
-        (long long)tpr * ppt * 16 < row_bytes ||
+        (long long)tpr * ppt < part ||
         (window != 1 && window != 2 && window != 3 && window != 8 && window != 16))
         return -1;
     if (rows == 0)
@@ -118,8 +130,10 @@ extern "C" __attribute__((visibility("default"))) int probe_rows(const void *con
             return -1;
         a.out[o] = out[o];
     }
-    a.P = row_bytes / 16;
+    a.P = P;
     a.tpr = tpr;
+    a.bpr = bpr;
+    a.part = part;
     hipError_t e;
     switch (nin) {
     case 2: e = go_p<2>(a, rows, ppt, window, st); break;
@@ -132,4 +146,12 @@ extern "C" __attribute__((visibility("default"))) int probe_rows(const void *con
     default: e = go_p<9>(a, rows, ppt, window, st); break;
     }
     return e == hipSuccess ? 0 : -4;
+}
+
+// probe_rows_split with one block per row.
+extern "C" __attribute__((visibility("default"))) int probe_rows(const void *const *in, int nin, void *const *out,
+                                                                 int nout, long long rows, int row_bytes, int ppt,
+                                                                 int tpr, int window, hipStream_t st)
+{
+    return probe_rows_split(in, nin, out, nout, rows, row_bytes, ppt, tpr, window, 1, st);
 }
