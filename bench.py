@@ -67,6 +67,7 @@ PEAK_GBS = 8000.0
 ROTATE_BYTES = 512 << 20
 PREROLL_CALLS = 4096
 PREROLL_SECONDS = 0.5
+CALIBRATE_BYTES = 256 << 20  # read and written by each calibration dispatch (--calibrate-copy)
 MAX_TIMED_CALLS = 4096       # small workloads: more timed calls, so that more distinct data is touched
 BANDWIDTH_BOUND_BYTES = 32 << 20   # per call: below this a launch is latency-bound (report us only)
 
@@ -112,8 +113,8 @@ def parse():
                    help="time the chosen workload inside graphs of --steps calls replayed back to back "
                         "(as every figure but the headline is), e.g. for kernel traces of latency-bound launches")
     p.add_argument("--calibrate-copy", action="store_true",
-                   help="also run a plain 256 MiB device-to-device copy (4 times) so that a "
-                        "profiler's FETCH_SIZE/WRITE_SIZE can be scaled by a kernel of known size")
+                   help="also run 4 dispatches of the probe kernel that each read and write 256 MiB, so "
+                        "that a profiler's FETCH_SIZE/WRITE_SIZE can be scaled by a kernel of known traffic")
     return p.parse_args()
 
 
@@ -622,6 +623,29 @@ def sweep(args):
     print(json.dumps({"sweep": args.sweep_out, "seconds": round(time.perf_counter() - t_start, 1)}), flush=True)
 
 
+def calibrate(torch):
+    """Four dispatches of the probe kernel (probe/libstream_probe.so), each
+    reading CALIBRATE_BYTES and writing CALIBRATE_BYTES (two 128 MiB inputs, two
+    128 MiB outputs): a kernel of known traffic, and the only probe dispatches of
+    a profiled run, by which prof.py scales FETCH_SIZE and WRITE_SIZE to bytes."""
+    lib = load_probe()
+    if lib is None:
+        raise SystemExit("--calibrate-copy needs probe/libstream_probe.so (python __graft_entry__.py)")
+    n = CALIBRATE_BYTES // 2
+    bufs = [torch.full((n,), 1, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    vp = ctypes.c_void_p
+    ins = (vp * 2)(bufs[0].data_ptr(), bufs[1].data_ptr())
+    outs = (vp * 2)(bufs[2].data_ptr(), bufs[3].data_ptr())
+    row_bytes = 16384
+    for _ in range(4):
+        rc = lib.probe_rows(ins, 2, outs, 2, n // row_bytes, row_bytes, 2, 512, 16,
+                            torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"probe_rows failed: {rc}")
+    torch.cuda.synchronize()
+    del bufs
+
+
 # ---- host facts -----------------------------------------------------------
 
 def read_clocks(torch):
@@ -738,12 +762,7 @@ def main():
     wl = wlmod.BY_NAME[args.workload]
     torch.cuda.set_device(0)
     if args.calibrate_copy:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(4):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibrate(torch)
     digest = sources_digest()
     if args.sum_only:
         case = wlmod.SUM_HEADLINE

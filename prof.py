@@ -5,9 +5,9 @@ Usage (paths are the rocprofv3 output directories of one command each):
       --workload NAME --path one --command "..." --out profiles/NAME.md
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
-counters read for a plain device-to-device copy of known size (bench.py
---calibrate-copy: 256 MiB read and 256 MiB written), so that the reported
-traffic is in bytes of HBM reads and writes.
+counters read for a kernel of known traffic (bench.py --calibrate-copy: four
+dispatches of the probe kernel, each reading 256 MiB and writing 256 MiB), so
+that the reported traffic is in bytes of HBM reads and writes.
 """
 from __future__ import annotations
 
@@ -69,9 +69,11 @@ def counter(dir_, name):
     return by
 
 
-def copy_kernel(names):
+def calibration_kernel(names):
+    """The calibration kernel (bench.py --calibrate-copy: the probe kernel, each
+    dispatch reading and writing COPY_BYTES), or None."""
     for n in names:
-        if "copyBuffer" in n or "copy" in n.lower():
+        if "probe_kernel" in n:
             return n
     return None
 
@@ -97,10 +99,10 @@ def main():
     ks = kernel_stats(a.trace)
     fetch = counter(a.fetch, "FETCH_SIZE") if a.fetch else {}
     write = counter(a.write, "WRITE_SIZE") if a.write else {}
-    ck = copy_kernel(fetch)
-    # the copy may be split into several dispatches: scale by the total over one copy
-    f_copy = sum(fetch[ck]) / 4.0 if ck else None
-    w_copy = sum(write.get(ck, [])) / 4.0 if ck else None
+    ck = calibration_kernel(fetch)
+    # each calibration dispatch reads and writes COPY_BYTES
+    f_copy = statistics.mean(fetch[ck]) if ck else None
+    w_copy = statistics.mean(write[ck]) if ck and write.get(ck) else None
     f_scale = COPY_BYTES / (f_copy * 1024.0) if f_copy else None
     w_scale = COPY_BYTES / (w_copy * 1024.0) if w_copy else None
     ours = [k for k in ks if "arrms::" in k]
@@ -123,10 +125,11 @@ def main():
         open(a.out, "w").write("\n".join(lines) + "\n")
         print("\n".join(lines))
         return
-    lines += ["", "HBM traffic per dispatch (counter KiB scaled by the 256 MiB copy's reading):", ""]
+    lines += ["", "HBM traffic per dispatch (counter KiB scaled by the calibration kernel's reading):", ""]
     if ck:
-        lines.append(f"- copy kernel `{ck}`: FETCH_SIZE {f_copy:.0f} KiB, WRITE_SIZE {w_copy:.0f} KiB per "
-                     f"256 MiB copy -> scale factors {f_scale:.4f} (reads), {w_scale:.4f} (writes)")
+        lines.append(f"- calibration kernel `{ck[:60]}` ({len(fetch[ck])} dispatches, each reading and writing "
+                     f"256 MiB): FETCH_SIZE {f_copy:.0f} KiB, WRITE_SIZE {w_copy:.0f} KiB per dispatch -> scale "
+                     f"factors {f_scale:.4f} (reads), {w_scale:.4f} (writes)")
     traffic = {}
     for k in ours:
         if k not in fetch:
