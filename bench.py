@@ -122,7 +122,10 @@ def sources_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "all_reduce_residual_rank_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+        path = os.path.join(csrc, name)
+        if not os.path.isfile(path):  # e.g. a Python cache directory
+            continue
+        with open(path, "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
