@@ -493,6 +493,12 @@ def load_probe():
     lib.probe_rows.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.POINTER(vp), ctypes.c_int,
                                ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     lib.probe_rows.restype = ctypes.c_int
+    lib.probe_rows_read.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, ctypes.c_longlong, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    lib.probe_rows_read.restype = ctypes.c_int
+    lib.probe_rows_write.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_longlong, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, vp]
+    lib.probe_rows_write.restype = ctypes.c_int
     return lib
 
 
@@ -500,7 +506,9 @@ def time_probe(torch, lib, wl, sets, steps, warmup, replays):
     """The probe over the workload's own rotating buffers: every row's R + 1 input
     streams read and two output streams written (residual_out and out), in the
     fused kernel's launch shape and load window, with no arithmetic; timed inside
-    graphs (time_graph_calls)."""
+    graphs (time_graph_calls). Also its two sides alone, each on the same
+    buffers and launch shape: the reads with nothing written, the writes with
+    nothing read."""
     from all_reduce_residual_rank_amd import arrms
     # the fused kernel's own launch shape and load window for this workload
     plan = arrms.arrms_query_launch(wl.M, wl.H, wl.R, wl.flags & ~arrms.FP8)
@@ -515,9 +523,27 @@ def time_probe(torch, lib, wl, sets, steps, warmup, replays):
         if rc != 0:
             raise RuntimeError(f"probe_rows failed: {rc}")
 
-    calls = [lambda st, d=d: one(d, st) for d in sets.sets]
-    us, us_min = time_graph_calls(torch, calls, max(steps, 64))
-    return {"us_per_call": us, "min_us": us_min,
+    sink = torch.zeros(max(wl.M, 1), dtype=torch.int32, device="cuda")
+
+    def read(d, st):
+        ins = (vp * (wl.R + 1))(*[x.data_ptr() for x in d["xs"]], d["res"].data_ptr())
+        rc = lib.probe_rows_read(ins, wl.R + 1, sink.data_ptr(), wl.M, wl.H * wl.esize, ppt, tpr, window,
+                                 st.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"probe_rows_read failed: {rc}")
+
+    def write(d, st):
+        outs = (vp * 2)(d["rout"].data_ptr(), d["out"].data_ptr())
+        rc = lib.probe_rows_write(outs, 2, wl.M, wl.H * wl.esize, ppt, tpr, st.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"probe_rows_write failed: {rc}")
+
+    n = max(steps, 64)
+    us, us_min = time_graph_calls(torch, [lambda st, d=d: one(d, st) for d in sets.sets], n)
+    rd_us, _ = time_graph_calls(torch, [lambda st, d=d: read(d, st) for d in sets.sets], n)
+    wr_us, _ = time_graph_calls(torch, [lambda st, d=d: write(d, st) for d in sets.sets], n)
+    del sink
+    return {"us_per_call": us, "min_us": us_min, "read_only_us": rd_us, "write_only_us": wr_us,
             "launch": {"packs_per_thread": ppt, "threads_per_row": tpr, "load_window": window}}
 
 
@@ -856,9 +882,15 @@ def main():
             kcalls = [lambda st, d=d: call(arrms, wl, d, wl.flags | path_flags[chosen], st) for d in sets.sets]
             ku, ku_min = time_graph_calls(torch, kcalls, max(args.steps, 64))
             line["graph_us_per_call"] = round(ku, 3)
+            rd_bytes = (wl.R + 1) * wl.M * wl.H * e
+            wr_bytes = 2 * wl.M * wl.H * e
             line["probe"] = {"kind": "data movement only: R+1 input and 2 output streams per row, no arithmetic",
                              "us_per_call": round(pu, 3), "min_us": round(pt["min_us"], 3),
                              "achieved": round(algo_bytes / (pu * 1e-6) / 1e9, 2), **pt["launch"],
+                             "read_only": {"us_per_call": round(pt["read_only_us"], 3),
+                                           "achieved": round(rd_bytes / (pt["read_only_us"] * 1e-6) / 1e9, 2)},
+                             "write_only": {"us_per_call": round(pt["write_only_us"], 3),
+                                            "achieved": round(wr_bytes / (pt["write_only_us"] * 1e-6) / 1e9, 2)},
                              "timing": "inside graphs, like graph_us_per_call"}
             line["probe_us"] = round(pu, 3)
             line["frac_of_probe"] = round(pu / ku, 4)

@@ -10,6 +10,11 @@
 // operation per word, so nothing is optimised away and no floating-point work is
 // done). Loads and stores are non-temporal, as in the fused kernel. Rows are
 // row_bytes long (a multiple of 16); packs past the row are skipped.
+//
+// Two one-sided forms bound the mix from either side: probe_rows_read reads the
+// same input streams in the same order and window and writes nothing but, in
+// practice never, one word per block (the loads stay live); probe_rows_write
+// writes the two output streams and reads nothing.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,6 +32,7 @@ struct ProbeArgs {
     int tpr;
     int bpr;  // blocks per row: block b takes part b % bpr of row b / bpr
     int part; // packs per part, ceil(P / bpr)
+    uint32_t *sink; // probe_rows_read: one word per block, written only if its XOR hits a fixed value
 };
 
 template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
@@ -68,31 +74,103 @@ __global__ void __launch_bounds__(1024) probe_kernel(const ProbeArgs a)
     }
 }
 
-template <int NIN, int PPT, int W> hipError_t go(const ProbeArgs &a, long long rows, hipStream_t st)
+// The read side alone: the same loads as probe_kernel, folded into one XOR per
+// thread; lane 0 of a block writes one word only when its XOR equals a fixed
+// value, which keeps every load live without output traffic.
+template <int NIN, int PPT, int W>
+__global__ void __launch_bounds__(1024) read_kernel(const ProbeArgs a)
 {
-    hipLaunchKernelGGL((probe_kernel<NIN, 2, PPT, W>), dim3((unsigned)(rows * a.bpr)), dim3(a.tpr), 0, st, a);
+    const long long row = blockIdx.x;
+    const int lt = threadIdx.x;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const int j = lt + k * a.tpr;
+        const int jc = j < a.P ? j : a.P - 1;
+#pragma unroll
+        for (int s = 0; s < NIN; ++s) {
+            acc ^= __builtin_nontemporal_load((const u32x4 *)a.in[s] + row * a.P + jc);
+            wait_vm<W - 1>();
+        }
+    }
+    wait_vm<0>();
+    const uint32_t v = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    if (lt == 0 && v == 0x9e3779b9u)
+        a.sink[blockIdx.x] = v;
+}
+
+// The write side alone: every pack of both output streams, values from the
+// indices.
+template <int PPT> __global__ void __launch_bounds__(1024) write_kernel(const ProbeArgs a)
+{
+    const long long row = blockIdx.x;
+    const int lt = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+        const int j = lt + k * a.tpr;
+        if (j >= a.P)
+            continue;
+        const u32x4 v = {(uint32_t)j, (uint32_t)row, 1u, 2u};
+        __builtin_nontemporal_store(v, (u32x4 *)a.out[0] + row * a.P + j);
+        __builtin_nontemporal_store(v, (u32x4 *)a.out[1] + row * a.P + j);
+    }
+}
+
+enum class Mode { Mix, Read };
+
+template <Mode MODE, int NIN, int PPT, int W> hipError_t go(const ProbeArgs &a, long long rows, hipStream_t st)
+{
+    if (MODE == Mode::Mix)
+        hipLaunchKernelGGL((probe_kernel<NIN, 2, PPT, W>), dim3((unsigned)(rows * a.bpr)), dim3(a.tpr), 0, st, a);
+    else
+        hipLaunchKernelGGL((read_kernel<NIN, PPT, W>), dim3((unsigned)rows), dim3(a.tpr), 0, st, a);
     return hipGetLastError();
 }
 
-template <int NIN, int PPT> hipError_t go_w(const ProbeArgs &a, long long rows, int window, hipStream_t st)
+template <Mode MODE, int NIN, int PPT>
+hipError_t go_w(const ProbeArgs &a, long long rows, int window, hipStream_t st)
 {
     switch (window) {
-    case 1: return go<NIN, PPT, 1>(a, rows, st);
-    case 2: return go<NIN, PPT, 2>(a, rows, st);
-    case 3: return go<NIN, PPT, 3>(a, rows, st);
-    case 8: return go<NIN, PPT, 8>(a, rows, st);
-    default: return go<NIN, PPT, 16>(a, rows, st);
+    case 1: return go<MODE, NIN, PPT, 1>(a, rows, st);
+    case 2: return go<MODE, NIN, PPT, 2>(a, rows, st);
+    case 3: return go<MODE, NIN, PPT, 3>(a, rows, st);
+    case 8: return go<MODE, NIN, PPT, 8>(a, rows, st);
+    default: return go<MODE, NIN, PPT, 16>(a, rows, st);
     }
 }
 
-template <int NIN> hipError_t go_p(const ProbeArgs &a, long long rows, int ppt, int window, hipStream_t st)
+template <Mode MODE, int NIN>
+hipError_t go_p(const ProbeArgs &a, long long rows, int ppt, int window, hipStream_t st)
 {
     switch (ppt) {
-    case 1: return go_w<NIN, 1>(a, rows, window, st);
-    case 2: return go_w<NIN, 2>(a, rows, window, st);
-    case 3: return go_w<NIN, 3>(a, rows, window, st);
-    default: return go_w<NIN, 4>(a, rows, window, st);
+    case 1: return go_w<MODE, NIN, 1>(a, rows, window, st);
+    case 2: return go_w<MODE, NIN, 2>(a, rows, window, st);
+    case 3: return go_w<MODE, NIN, 3>(a, rows, window, st);
+    default: return go_w<MODE, NIN, 4>(a, rows, window, st);
     }
+}
+
+template <Mode MODE>
+hipError_t go_n(const ProbeArgs &a, long long rows, int nin, int ppt, int window, hipStream_t st)
+{
+    switch (nin) {
+    case 2: return go_p<MODE, 2>(a, rows, ppt, window, st);
+    case 3: return go_p<MODE, 3>(a, rows, ppt, window, st);
+    case 4: return go_p<MODE, 4>(a, rows, ppt, window, st);
+    case 5: return go_p<MODE, 5>(a, rows, ppt, window, st);
+    case 6: return go_p<MODE, 6>(a, rows, ppt, window, st);
+    case 7: return go_p<MODE, 7>(a, rows, ppt, window, st);
+    case 8: return go_p<MODE, 8>(a, rows, ppt, window, st);
+    default: return go_p<MODE, 9>(a, rows, ppt, window, st);
+    }
+}
+
+// Shape rules of the one-block-per-row forms (the read and write probes).
+bool shape_ok(long long rows, int row_bytes, int ppt, int tpr, int window)
+{
+    return rows >= 0 && rows <= 0x7fffffffLL && row_bytes >= 16 && row_bytes % 16 == 0 && ppt >= 1 && ppt <= 4 &&
+           tpr >= 64 && tpr <= 1024 && tpr % 64 == 0 && (long long)tpr * ppt >= row_bytes / 16 &&
+           (window == 1 || window == 2 || window == 3 || window == 8 || window == 16);
 }
 
 }  // namespace
@@ -134,18 +212,7 @@ extern "C" __attribute__((visibility("default"))) int probe_rows_split(const voi
     a.tpr = tpr;
     a.bpr = bpr;
     a.part = part;
-    hipError_t e;
-    switch (nin) {
-    case 2: e = go_p<2>(a, rows, ppt, window, st); break;
-    case 3: e = go_p<3>(a, rows, ppt, window, st); break;
-    case 4: e = go_p<4>(a, rows, ppt, window, st); break;
-    case 5: e = go_p<5>(a, rows, ppt, window, st); break;
-    case 6: e = go_p<6>(a, rows, ppt, window, st); break;
-    case 7: e = go_p<7>(a, rows, ppt, window, st); break;
-    case 8: e = go_p<8>(a, rows, ppt, window, st); break;
-    default: e = go_p<9>(a, rows, ppt, window, st); break;
-    }
-    return e == hipSuccess ? 0 : -4;
+    return go_n<Mode::Mix>(a, rows, nin, ppt, window, st) == hipSuccess ? 0 : -4;
 }
 
 // probe_rows_split with one block per row.
@@ -154,4 +221,54 @@ extern "C" __attribute__((visibility("default"))) int probe_rows(const void *con
                                                                  int tpr, int window, hipStream_t st)
 {
     return probe_rows_split(in, nin, out, nout, rows, row_bytes, ppt, tpr, window, 1, st);
+}
+
+// The read side of probe_rows alone (one block per row): in as for probe_rows;
+// sink: rows 32-bit words of device memory (written, in practice, never).
+extern "C" __attribute__((visibility("default"))) int probe_rows_read(const void *const *in, int nin, void *sink,
+                                                                      long long rows, int row_bytes, int ppt, int tpr,
+                                                                      int window, hipStream_t st)
+{
+    if (nin < 2 || nin > kMaxIn || !sink || !shape_ok(rows, row_bytes, ppt, tpr, window))
+        return -1;
+    if (rows == 0)
+        return 0;
+    ProbeArgs a = {};
+    for (int s = 0; s < nin; ++s) {
+        if (!in[s])
+            return -1;
+        a.in[s] = in[s];
+    }
+    a.sink = (uint32_t *)sink;
+    a.P = row_bytes / 16;
+    a.tpr = tpr;
+    a.bpr = 1;
+    a.part = a.P;
+    return go_n<Mode::Read>(a, rows, nin, ppt, window, st) == hipSuccess ? 0 : -4;
+}
+
+// The write side of probe_rows alone (one block per row): out: nout (= 2)
+// device pointers to rows x row_bytes.
+extern "C" __attribute__((visibility("default"))) int probe_rows_write(void *const *out, int nout, long long rows,
+                                                                       int row_bytes, int ppt, int tpr,
+                                                                       hipStream_t st)
+{
+    if (nout != 2 || !out[0] || !out[1] || !shape_ok(rows, row_bytes, ppt, tpr, 2))
+        return -1;
+    if (rows == 0)
+        return 0;
+    ProbeArgs a = {};
+    a.out[0] = out[0];
+    a.out[1] = out[1];
+    a.P = row_bytes / 16;
+    a.tpr = tpr;
+    a.bpr = 1;
+    a.part = a.P;
+    switch (ppt) {
+    case 1: hipLaunchKernelGGL((write_kernel<1>), dim3((unsigned)rows), dim3(tpr), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((write_kernel<2>), dim3((unsigned)rows), dim3(tpr), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((write_kernel<3>), dim3((unsigned)rows), dim3(tpr), 0, st, a); break;
+    default: hipLaunchKernelGGL((write_kernel<4>), dim3((unsigned)rows), dim3(tpr), 0, st, a); break;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -4;
 }
