@@ -4,8 +4,8 @@ One step = one arrms_fused call over the headline workload (R=4 rank inputs,
 1024 x 6144 bf16 rows, per-row input scales, plain RMSNorm, bf16 output),
 with its inputs already resident in HBM. The timed calls cycle through enough
 rotating buffer sets (>= 512 MiB in total, twice the 256 MB Infinity Cache) that
-every call reads cold data from HBM. Calls are captured in a HIP graph and
-timed with HIP events on the stream the kernels run on.
+every call reads cold data from HBM. Calls are timed with HIP events on the
+stream the kernels run on, as the protocol below describes.
 
 Timing protocol (every figure below):
   pre-roll    the timed graph itself is replayed, untimed, until at least
@@ -34,7 +34,8 @@ Prints one JSON line:
               measured kernel duration, against MI355X's 8 TB/s HBM peak
   probe       a data-movement-only kernel over the same bytes (5 read and 2 write
               streams per row, no arithmetic), the measured ceiling the fused
-              kernel is compared with (frac_of_probe)
+              kernel is compared with (frac_of_probe); with its read side and
+              its write side timed alone on the same buffers
   workloads   every workload of the scope table (the 16-row decode case, the
               headline on both paths, the FP8 workload, the R=8 wide rows on both
               paths, the tail/decode sweep) with us/call per path

@@ -53,7 +53,7 @@ extern "C" {
 #define ARRMS_QUANT_FP8_TOKEN 1    /* per-token FP8: as arrms_fused with ARRMS_FP8 */
 #define ARRMS_QUANT_FP8_GROUP 2    /* per-group FP8: E4M3 codes [M][H], fp32 scales [M][H/128] */
 #define ARRMS_QUANT_MXFP4 3        /* MXFP4: packed E2M1 codes [M][H/2], E8M0 scales [M][H/32] */
-#define ARRMS_FP8_GROUP_SIZE 128   /* columns per per-group FP8 scale */
+#define ARRMS_FP8_GROUP_SIZE 128   /* columns per per-group FP8 scale (no page fixes it; see arrms_fused_quant) */
 #define ARRMS_MX_BLOCK 32          /* columns per MXFP4 scale (OCP MX block size) */
 
 /* ---- limits -------------------------------------------------------------- */
@@ -176,7 +176,9 @@ ARRMS_API int arrms_fused_strided(const void *const *rank_in, int R, const void 
  * per-group and the MXFP4 quant forms). The pages do not define the last two;
  * this library reads them as:
  *   ARRMS_QUANT_FP8_GROUP  the per-token FP8 steps on each group of
- *       ARRMS_FP8_GROUP_SIZE (128) consecutive columns: scale = fl32(gmax /
+ *       ARRMS_FP8_GROUP_SIZE (128) consecutive columns -- no page gives a
+ *       group size: 128 is this library's choice (the usual 1 x 128
+ *       activation grouping), not a reading of the pages: scale = fl32(gmax /
  *       448) over the T-rounded y of the group, q = E4M3_RNE_sat(fl32(y /
  *       scale)), an all-zero group gives scale 0 and signed zeros, a NaN
  *       in the group a NaN scale and codes 0x7F.

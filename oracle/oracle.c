@@ -33,7 +33,9 @@
  * (PR #6699 Motivation and Changes) without defining them; this oracle
  * reads them as:
  *   O6  per-group FP8: O5's steps on each group of 128 consecutive
- *       columns (scales [M][H/128] fp32);
+ *       columns (scales [M][H/128] fp32). No page gives a group size:
+ *       128 (the usual 1 x 128 activation grouping) is a choice, and the
+ *       pins hold O6 to this reading only;
  *   O7  MXFP4 (OCP Microscaling Formats v1.0, MXFP4): blocks of 32
  *       columns, E8M0 scale X = 2^(floor(log2(amax)) - 2), elements
  *       E2M1_RNE_sat(y / X), two per byte with the even column in the low
