@@ -43,6 +43,15 @@ public:
         Dev &d = d_[dev];
         if (d.ptr && d.bytes >= bytes)
             return 0;
+        if (d.ptr) {
+            // room for the retired entry first, so that nothing below can throw
+            // (no exception may cross the C ABI)
+            try {
+                d.retired.reserve(d.retired.size() + 1);
+            } catch (...) {
+                return -1;
+            }
+        }
         void *p = nullptr;
         if (ops_.alloc(&p, bytes) != 0 || !p)
             return -1;
