@@ -16,11 +16,12 @@ Timing protocol (every figure below):
   timed       exactly --steps calls of the entry point, eager, on one stream,
               between two HIP events. Each block of timed calls is queued behind
               untimed filler on the same stream (replays of a graph of the same
-              calls), long enough that the host has issued the whole block
-              before the GPU reaches its first event: the figure is the GPU time
-              of back-to-back calls, with no host launch gap and no per-graph
-              launch cost inside. Further blocks, queued the same way, give the
-              spread (replays). This is the headline's own measurement; every
+              calls, then LEAD_IN_CALLS eager calls), long enough that the host
+              has issued the whole block before the GPU reaches its first event:
+              the figure is the GPU time of back-to-back calls, with no host
+              launch gap and no per-graph launch cost inside. Every block starts
+              at the first buffer set. Further blocks, each queued the same way
+              after the previous one has finished, give the spread (replays). This is the headline's own measurement; every
               other figure (other workloads and paths, the quant forms, the sum,
               the probe, the sweep) is the us per call inside graphs of at least
               64 calls replayed back to back (time_graph_calls), because the
@@ -68,6 +69,7 @@ PEAK_GBS = 8000.0
 ROTATE_BYTES = 512 << 20
 PREROLL_CALLS = 4096
 PREROLL_SECONDS = 0.5
+LEAD_IN_CALLS = 4            # untimed eager calls between the filler and each timed block
 CALIBRATE_BYTES = 256 << 20  # read and written by each calibration dispatch (--calibrate-copy)
 MAX_TIMED_CALLS = 4096       # small workloads: more timed calls, so that more distinct data is touched
 BANDWIDTH_BOUND_BYTES = 32 << 20   # per call: below this a launch is latency-bound (report us only)
@@ -215,11 +217,13 @@ def time_calls(torch, calls, steps, warmup, replays=0, ncalls=None, preroll=(PRE
 
     The timed calls are ordinary eager calls of the entry point on one stream.
     Before each block the stream gets untimed filler -- replays of a graph of
-    the same calls -- long enough (twice the host's time to issue the block)
-    that the host has queued the whole block before the GPU reaches its first
-    event: the events see back-to-back execution only, with no host launch gap
-    and no per-graph launch cost inside. Returns us per call of the first block,
-    the spread of the others and the pre-roll count."""
+    the same calls, then a few eager calls -- long enough (twice the host's
+    time to issue them and the block) that the host has queued the whole block
+    before the GPU reaches its first event: the events see back-to-back
+    execution only, with no host launch gap and no per-graph launch cost
+    inside. Each block starts at the first of `calls` and is queued once the
+    previous one has finished. Returns us per call of the first block, the
+    spread of the others and the pre-roll count."""
     ncalls = steps if ncalls is None else ncalls
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -235,20 +239,27 @@ def time_calls(torch, calls, steps, warmup, replays=0, ncalls=None, preroll=(PRE
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     h_call = statistics.median(host)
-    nfill = max(1, -(-int((2.0 * ncalls * h_call + 200e-6) * 1e6) // int(g.gpu_s * 1e6)))
-    blocks = []
+    lead = min(LEAD_IN_CALLS, len(calls))
+    nfill = max(1, -(-int((2.0 * (ncalls + lead) * h_call + 200e-6) * 1e6) // int(g.gpu_s * 1e6)))
+    us = []
     with torch.cuda.stream(s):
         for b in range(1 + replays):
+            # filler, then a few untimed eager calls (the first eager launches
+            # after a graph replay are not yet back to back), then the block.
+            # Every block starts at the first buffer set, so all blocks read the
+            # same mix of sets, and the device is synchronised after each block,
+            # so the host queues each block against an empty queue.
             g.replay(nfill)
+            for i in range(lead):
+                calls[(len(calls) - lead + i) % len(calls)](s)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(s)
             for i in range(ncalls):
-                calls[(b * ncalls + i) % len(calls)](s)
+                calls[i % len(calls)](s)
             e1.record(s)
-            blocks.append((e0, e1))
-    torch.cuda.synchronize()
-    us = [a.elapsed_time(z) * 1000.0 / ncalls for a, z in blocks]
+            torch.cuda.synchronize()
+            us.append(e0.elapsed_time(e1) * 1000.0 / ncalls)
     out = {"us_per_call": us[0], "preroll_calls": pre, "warmup_calls": max(warmup, 16), "calls_per_block": ncalls,
            "host_us_per_call": round(h_call * 1e6, 1), "filler_calls": nfill * g.ncalls}
     if replays:

@@ -84,8 +84,8 @@ def main():
     ap.add_argument("--fetch", help="rocprofv3 --pmc FETCH_SIZE output (omit for a trace-only summary)")
     ap.add_argument("--write", help="rocprofv3 --pmc WRITE_SIZE output")
     ap.add_argument("--last", type=int, default=0,
-                    help="also summarise the last N dispatches of the library's kernels (the timed graph "
-                         "replays): durations, start-to-start spacing, idle gap between kernels")
+                    help="also summarise the last N dispatches of the library's kernels (the end of the timed "
+                         "part of the run): durations, start-to-start spacing, idle gap between kernels")
     ap.add_argument("--workload", required=True)
     ap.add_argument("--path", required=True)
     ap.add_argument("--command", required=True)
@@ -112,15 +112,16 @@ def main():
             ([f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- {a.command}",
               f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- {a.command}"] if a.fetch else []) + \
             ["```", "",
-             f"Kernel sources digest: `{a.digest}`. bench.py us/call of the same command: {a.bench_us:.3f}.",
+             f"Kernel sources digest: `{a.digest}`. bench.py us/call of the same command, under the profiler "
+             f"(which adds its own cost to every launch): {a.bench_us:.3f}.",
              "", "| kernel | dispatches | avg us | median us | min us | max us |", "|---|---|---|---|---|---|"]
     for k in sorted(ks, key=lambda k: -ks[k]["avg_ns"] * ks[k]["count"]):
         v = ks[k]
         lines.append(f"| `{k[:90]}` | {v['count']} | {v['avg_ns']/1e3:.3f} | {v['median_ns']/1e3:.3f} | "
                      f"{v['min_ns']/1e3:.3f} | {v['max_ns']/1e3:.3f} |")
     if a.last:
-        lines += ["", f"The last {a.last} dispatches of the library's kernels (the timed graph replays, calls back "
-                  "to back):", ""] + last_dispatches(a.trace, a.last)
+        lines += ["", f"The last {a.last} dispatches of the library's kernels (the end of the timed part of the "
+                  "run):", ""] + last_dispatches(a.trace, a.last)
     if not a.fetch:
         open(a.out, "w").write("\n".join(lines) + "\n")
         print("\n".join(lines))
