@@ -1,8 +1,11 @@
-"""Summaries of rocprofv3 runs of bench.py: per-kernel durations and HBM traffic.
+"""Summaries of rocprofv3 runs of bench.py: per-kernel durations and HBM traffic,
+and issue counters.
 
 Usage (paths are the rocprofv3 output directories of one command each):
   python prof.py --trace DIR --fetch DIR --write DIR \\
       --workload NAME --path one --command "..." --out profiles/NAME.md
+  python prof.py counters DIR [DIR ...] --title "..." --command "..." [--command ...] \\
+      --digest D --out profiles/NAME.md
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
 counters read for a kernel of known traffic (bench.py --calibrate-copy: four
@@ -17,6 +20,7 @@ import glob
 import json
 import os
 import statistics
+import sys
 
 COPY_BYTES = 256 << 20
 
@@ -78,7 +82,75 @@ def calibration_kernel(names):
     return None
 
 
+def counter_medians(dirs):
+    """{kernel: {counter: median over its dispatches}} over rocprofv3 --pmc output
+    directories (one counter set each), for the library's kernels."""
+    out = {}
+    for d in dirs:
+        by = {}
+        for r in _csv(d, "counter_collection.csv"):
+            if "arrms::" not in r["Kernel_Name"]:
+                continue
+            by.setdefault((r["Kernel_Name"], r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+        for (k, c), v in by.items():
+            out.setdefault(k, {})[c] = statistics.median(v)
+    return out
+
+
+def derived(cs):
+    """Per-wave and per-cycle figures from the issue counters (whichever are there)."""
+    d = {}
+    w = cs.get("SQ_WAVES")
+    if w:
+        for c, name in (("SQ_INSTS_VALU", "VALU instructions per wave"), ("SQ_INSTS_SALU", "SALU instructions per wave"),
+                        ("SQ_INSTS_VMEM_RD", "vector memory reads per wave"),
+                        ("SQ_INSTS_VMEM_WR", "vector memory writes per wave"),
+                        ("SQ_WAVE_CYCLES", "wave lifetime, cycles")):
+            if c in cs:
+                d[name] = cs[c] / w
+    wc = cs.get("SQ_WAVE_CYCLES")
+    if wc:
+        for c, name in (("SQ_WAIT_INST_ANY", "share of wave cycles waiting for an issue slot"),
+                        ("SQ_WAIT_ANY", "share of wave cycles waiting on memory or a dependency")):
+            if c in cs:
+                d[name] = cs[c] / wc
+    return d
+
+
+def counters_main(argv):
+    ap = argparse.ArgumentParser(prog="prof.py counters",
+                                 description="Median issue counters of the library's kernels, one pass per directory")
+    ap.add_argument("dirs", nargs="+", help="rocprofv3 --pmc output directories")
+    ap.add_argument("--title", required=True)
+    ap.add_argument("--command", action="append", required=True,
+                    help="the profiled command of each pass, in the order of dirs")
+    ap.add_argument("--digest", required=True)
+    ap.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    med = counter_medians(a.dirs)
+    kernels = sorted(med)
+    names = sorted({c for k in kernels for c in med[k]})
+    lines = [f"# rocprofv3 counters: {a.title}", "", "One counter pass per run (run from the repository root):", "",
+             "```"] + a.command + ["```", "", f"Kernel sources digest: `{a.digest}`. Values: median over the "
+             "dispatches of each kernel of the counter summed over the device's instances. Under counter collection "
+             "kernels run slower than in bench.py, so cycle counts are compared per wave and as ratios, not as times.",
+             "", "| counter | " + " | ".join(f"`{k[:60]}`" for k in kernels) + " |",
+             "|---|" + "---|" * len(kernels)]
+    for c in names:
+        lines.append(f"| {c} | " + " | ".join(f"{med[k].get(c, float('nan')):.0f}" for k in kernels) + " |")
+    lines += ["", "Derived:", ""]
+    for k in kernels:
+        dv = derived(med[k])
+        lines.append(f"- `{k[:60]}`: " + "; ".join(f"{n} {v:.3f}" if n.startswith("share") else f"{n} {v:.1f}"
+                                                  for n, v in dv.items()))
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "counters":
+        counters_main(sys.argv[2:])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--trace", required=True)
     ap.add_argument("--fetch", help="rocprofv3 --pmc FETCH_SIZE output (omit for a trace-only summary)")
