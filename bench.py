@@ -748,7 +748,7 @@ def cpu_baseline(wl, budget_s):
            "us_per_row": round(t / rows * 1e6, 3)}
     # the same sample split by rows over the host's cores (the oracle's C code
     # runs outside the GIL), for context: every core of the process's affinity
-    # mask, at most 16 (the CPU share of one GPU on the GPU machine)
+    # mask, at most 16 (a host's CPU share for one GPU)
     from concurrent.futures import ThreadPoolExecutor
     n = max(1, min(len(os.sched_getaffinity(0)), 16, rows))
     bounds = [(rows * i // n, rows * (i + 1) // n) for i in range(n)]
