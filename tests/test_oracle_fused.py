@@ -81,7 +81,7 @@ def test_constant_row_closed_form(dt, c):
             code = fmt_ref.nearest_fraction(exact, table)
             got = int(o["out"][0, j]) & 0x7FFF
             assert got == code, (j, c)
-            # and the spec form: w * sign(c) (|c| >> sqrt(eps))
+            # and the closed form w * sign(c) (|c| >> sqrt(eps))
             assert values(o["out"][0:1, j], dt)[0] == float(wv[j]) * np.sign(c)
 
 
