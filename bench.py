@@ -590,7 +590,11 @@ def sweep(args):
     Rs = [int(x) for x in args.sweep_r.split(",")]
     kinds = args.sweep_kinds.split(",")
     os.makedirs(os.path.dirname(os.path.abspath(args.sweep_out)), exist_ok=True)
-    f = open(args.sweep_out, "w", newline="")
+    # rows go to <out>.partial as they are measured (a run that is cut short
+    # leaves what it has there) and the file takes its final name only when the
+    # sweep is complete
+    partial = args.sweep_out + ".partial"
+    f = open(partial, "w", newline="")
     wr = csv.DictWriter(f, fieldnames=SWEEP_FIELDS)
     wr.writeheader()
     gen = torch.Generator(device=dev)
@@ -661,6 +665,7 @@ def sweep(args):
                     del sets
                     torch.cuda.empty_cache()
     f.close()
+    os.replace(partial, args.sweep_out)
     print(json.dumps({"sweep": args.sweep_out, "seconds": round(time.perf_counter() - t_start, 1)}), flush=True)
 
 

@@ -25,6 +25,15 @@ import sys
 COPY_BYTES = 256 << 20
 
 
+def write_atomic(path, text):
+    """Write text to path through a temporary file and a rename, so that a
+    reader never sees a half-written file."""
+    tmp = path + ".tmp"
+    with open(tmp, "w") as f:
+        f.write(text)
+    os.replace(tmp, path)
+
+
 def _csv(d, suffix):
     f = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
     if not f:
@@ -143,7 +152,7 @@ def counters_main(argv):
         dv = derived(med[k])
         lines.append(f"- `{k[:60]}`: " + "; ".join(f"{n} {v:.3f}" if n.startswith("share") else f"{n} {v:.1f}"
                                                   for n, v in dv.items()))
-    open(a.out, "w").write("\n".join(lines) + "\n")
+    write_atomic(a.out, "\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
@@ -195,7 +204,7 @@ def main():
         lines += ["", f"The last {a.last} dispatches of the library's kernels (the end of the timed part of the "
                   "run):", ""] + last_dispatches(a.trace, a.last)
     if not a.fetch:
-        open(a.out, "w").write("\n".join(lines) + "\n")
+        write_atomic(a.out, "\n".join(lines) + "\n")
         print("\n".join(lines))
         return
     lines += ["", "HBM traffic per dispatch (counter KiB scaled by the calibration kernel's reading):", ""]
@@ -212,7 +221,7 @@ def main():
         lines.append(f"- `{k[:90]}`: reads {fr/1e6:.2f} MB, writes {wr/1e6:.2f} MB, total {(fr+wr)/1e6:.2f} MB "
                      f"(algorithmic {a.algo_bytes/1e6:.2f} MB per call)")
         traffic[k] = fr + wr
-    open(a.out, "w").write("\n".join(lines) + "\n")
+    write_atomic(a.out, "\n".join(lines) + "\n")
     db = {}
     if os.path.exists(a.traffic_json):
         db = json.load(open(a.traffic_json))
@@ -220,7 +229,7 @@ def main():
                                      "hbm_bytes_per_launch": round(sum(traffic.values())),
                                      "per_kernel_bytes": {k[:90]: round(v) for k, v in traffic.items()},
                                      "summary": os.path.basename(a.out)}
-    json.dump(db, open(a.traffic_json, "w"), indent=1)
+    write_atomic(a.traffic_json, json.dumps(db, indent=1))
     print("\n".join(lines))
 
 
