@@ -206,7 +206,7 @@ int choose_path(int M, int H, int R, int flags)
     // in, two outputs); two-stage adds a staging write and read. Measured: at
     // none of the 324 points of the launch-shape sweep (rows 1-4096, hidden
     // 512-8192, 2/4/8 ranks, bf16 T output and fp16 per-token FP8) is it the
-    // fastest; it takes 1.18 to 2 times the best one-stage launch.
+    // fastest; it takes 1.18 to 2.6 times the best one-stage launch.
     return ARRMS_PATH_ONE_STAGE;
 }
 

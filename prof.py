@@ -5,7 +5,7 @@ Usage (paths are the rocprofv3 output directories of one command each):
   python prof.py --trace DIR --fetch DIR --write DIR \\
       --workload NAME --path one --command "..." --out profiles/NAME.md
   python prof.py counters DIR [DIR ...] --title "..." --command "..." [--command ...] \\
-      --digest D --out profiles/NAME.md
+      --build B --out profiles/NAME.md
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what the same
 counters read for a kernel of known traffic (bench.py --calibrate-copy: four
@@ -133,14 +133,15 @@ def counters_main(argv):
     ap.add_argument("--title", required=True)
     ap.add_argument("--command", action="append", required=True,
                     help="the profiled command of each pass, in the order of dirs")
-    ap.add_argument("--digest", required=True)
+    ap.add_argument("--build", required=True, help="first 16 hex digits of the SHA-256 of libarrms.so")
     ap.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     med = counter_medians(a.dirs)
     kernels = sorted(med)
     names = sorted({c for k in kernels for c in med[k]})
     lines = [f"# rocprofv3 counters: {a.title}", "", "One counter pass per run (run from the repository root):", "",
-             "```"] + a.command + ["```", "", f"Kernel sources digest: `{a.digest}`. Values: median over the "
+             "```"] + a.command + ["```", "", f"Library build (SHA-256 of libarrms.so, first 16 hex digits): `{a.build}`. "
+             "Values: median over the "
              "dispatches of each kernel of the counter summed over the device's instances. Under counter collection "
              "kernels run slower than in bench.py, so cycle counts are compared per wave and as ratios, not as times.",
              "", "| counter | " + " | ".join(f"`{k[:60]}`" for k in kernels) + " |",
@@ -170,7 +171,8 @@ def main():
     ap.add_argument("--workload", required=True)
     ap.add_argument("--path", required=True)
     ap.add_argument("--command", required=True)
-    ap.add_argument("--digest", required=True)
+    ap.add_argument("--build", required=True, help="the library build profiled: first 16 hex digits of the "
+                    "SHA-256 of libarrms.so (bench.library_build())")
     ap.add_argument("--algo-bytes", type=int, required=True)
     ap.add_argument("--bench-us", type=float, required=True, help="bench.py us/call of the same command")
     ap.add_argument("--out", required=True)
@@ -193,7 +195,8 @@ def main():
             ([f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- {a.command}",
               f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- {a.command}"] if a.fetch else []) + \
             ["```", "",
-             f"Kernel sources digest: `{a.digest}`. bench.py us/call of the same command, under the profiler "
+             f"Library build (SHA-256 of libarrms.so, first 16 hex digits): `{a.build}`. bench.py us/call of the "
+             f"same command, under the profiler "
              f"(which adds its own cost to every launch): {a.bench_us:.3f}.",
              "", "| kernel | dispatches | avg us | median us | min us | max us |", "|---|---|---|---|---|---|"]
     for k in sorted(ks, key=lambda k: -ks[k]["avg_ns"] * ks[k]["count"]):
@@ -225,7 +228,7 @@ def main():
     db = {}
     if os.path.exists(a.traffic_json):
         db = json.load(open(a.traffic_json))
-    db[f"{a.workload}/{a.path}"] = {"sources_digest": a.digest,
+    db[f"{a.workload}/{a.path}"] = {"library_build": a.build,
                                      "hbm_bytes_per_launch": round(sum(traffic.values())),
                                      "per_kernel_bytes": {k[:90]: round(v) for k, v in traffic.items()},
                                      "summary": os.path.basename(a.out)}
